@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-expert MoE layer on one MI355X.
+
+Default workload: batch-1 decode (T=1 token per step; d=4096, I=2048, E=256
+routed experts with affine 4-bit g64 weights, top-6, plus the always-on shared
+expert in affine 8-bit g64; 64 seeded activation steps). A step is one
+moe_forward (route, bucket, experts, combine) of one batch.
+
+Timed region: K steps captured in one HIP graph and replayed once, between a
+torch.cuda.synchronize() on each side; inputs and weights are resident in HBM.
+Steps rotate over several device copies of the layer so that no step finds its
+weights in the 256 MB Infinity Cache left there by a recent step.
+
+Also reported: the dominant kernel's roofline from HIP events recorded on the
+library's stream between kernels (moe_forward_probed), and the CPU oracle timed
+on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill)"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=256)
+    p.add_argument("--warmup", type=int, default=16)
+    p.add_argument("--workload", default="decode", choices=["decode", "tiny", "hash", "prefill", "mixed"])
+    p.add_argument("--copies", type=int, default=0, help="device copies of the layer to rotate over (0: auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
+    p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    return p.parse_args()
+
+
+def workload_text(cfg) -> str:
+    def fmt(f):
+        return "mxfp4 e2m1+e8m0/32" if f.fmt == "mxfp4" else f"affine {f.bits}-bit g{f.group}"
+    s = (f"{cfg.name}: T={cfg.T} tokens/step, d={cfg.d}, I={cfg.I}, E={cfg.E}, top-{cfg.top_k} "
+         f"{'tid2eid hash' if cfg.route == 'hash' else 'sqrtsoftplus+bias'} routing, gate/up {fmt(cfg.gate_up)}, "
+         f"down {fmt(cfg.down)}")
+    if cfg.shared is not None:
+        s += f", shared expert I={cfg.I_shared} {fmt(cfg.shared)}"
+    return s + f", {cfg.steps} seeded activation batch(es)"
+
+
+def kernel_bytes(name, cfg, dl, T, touched):
+    """Algorithmic HBM bytes of one launch: the weights the kernel must read
+    (touched experts only) plus its activation inputs and outputs."""
+    k, d, E, I = cfg.top_k, cfg.d, cfg.E, cfg.I
+    r = dl.routed
+    sh = dl.shared
+    tk = T * k
+    if name == "router_logits":
+        return E * d * 4 + T * d * 2 + T * E * 4
+    if name == "router_topk":
+        return T * E * 4 + E * 4 + tk * 8
+    if name == "router_hash":
+        return min(E, tk) * d * 4 + T * d * 2 + T * 4 + tk * 4 + tk * 8
+    if name == "permute":
+        return tk * 4 + (E + 1) * 4 + tk * 4
+    if name == "routed_gateup":
+        return touched * (r.gate.nbytes_per_expert() + r.up.nbytes_per_expert()) + T * d * 2 + tk * I * 2
+    if name == "routed_down":
+        return touched * r.down.nbytes_per_expert() + tk * I * 2 + tk * d * 4
+    if name == "shared_gateup":
+        return sh.gate.nbytes_per_expert() + sh.up.nbytes_per_expert() + T * d * 2 + T * cfg.I_shared * 2
+    if name == "shared_down":
+        return sh.down.nbytes_per_expert() + T * cfg.I_shared * 2 + T * d * 4
+    if name == "combine":
+        return tk * d * 4 + tk * 4 + (T * d * 4 if sh is not None else 0) + T * d * 2
+    raise KeyError(name)
+
+
+def step_bytes(cfg, dl, T, touched):
+    """Algorithmic bytes of a whole step: touched routed experts, shared
+    expert, router weights, activations in and out."""
+    b = touched * dl.routed.nbytes_per_expert() + cfg.E * cfg.d * 4 + T * cfg.d * 2 * 2
+    if dl.shared is not None:
+        b += dl.shared.nbytes_per_expert()
+    return b
+
+
+def cpu_baseline(cfg, layer, xs, toks, target_s):
+    """The float64 oracle, as it stands, on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    n_tok = 0
+    steps = 0
+    t0 = time.perf_counter()
+    T_sample = cfg.T if cfg.T <= 4 else 2
+    while True:
+        s = steps % len(xs)
+        x = xs[s][:T_sample]
+        tok = None if toks is None else toks[s][:T_sample]
+        oracle.forward(layer, x, token_ids=tok)
+        n_tok += x.shape[0]
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or steps >= 64:
+            break
+    sample = (f"{steps} oracle forward call(s) of {T_sample} token(s) each on the same workload "
+              f"(each call dequantises its touched experts to float64), {el:.1f} s")
+    return {"value": n_tok / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": sample, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import quantized_sparse_moe_amd as qm
+    import synth
+
+    qm.load()  # fails loudly if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.config(args.workload)
+    T = cfg.T
+
+    t_gen = time.perf_counter()
+    layer = synth.gen_layer(cfg)
+    base = qm.DeviceLayer.from_host(layer, dev)
+    per_step_guess = step_bytes(cfg, base, T, min(cfg.E, T * cfg.top_k))
+    copies = args.copies or max(1, min(8, math.ceil(1.0e9 / per_step_guess)))
+    layers = [base] + [base.clone() for _ in range(copies - 1)]
+    n_x = max(1, cfg.steps)
+    xs_host = [synth.gen_x(cfg, s) for s in range(n_x)]
+    toks_host = [synth.gen_token_ids(cfg, s) for s in range(n_x)] if cfg.route == "hash" else None
+    xs = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs_host]
+    toks = [torch.from_numpy(t).to(dev) for t in toks_host] if toks_host else [None] * n_x
+    ws = base.workspace(T)
+    out = torch.empty((T, cfg.d), dtype=torch.bfloat16, device=dev)
+    gen_s = time.perf_counter() - t_gen
+
+    # distinct experts touched per activation batch (same for every layer copy)
+    touched = []
+    for i in range(n_x):
+        ids, _ = qm.route(base, xs[i], toks[i], ws)
+        touched.append(int(torch.unique(ids).numel()))
+    touched_mean = float(np.mean(touched))
+
+    def step(i):
+        qm.forward(layers[i % copies], xs[i % n_x], toks[i % n_x], ws=ws, out=out)
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    assert qm.device_error(ws) == 0
+
+    mode = "eager" if args.eager else "hipgraph"
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                for i in range(K):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        graph.replay()  # untimed
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if args.eager:
+        for i in range(K):
+            step(i)
+    else:
+        graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / K
+    assert qm.device_error(ws) == 0
+
+    # per-kernel durations: events between kernels, host kept ahead of the GPU
+    n_ev = 17
+    probe_steps = min(K, 64)
+    sums = {}
+    for i in range(probe_steps):
+        torch.cuda._sleep(2_000_000)  # lets the host enqueue the step before it runs
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        names = qm.forward_probed(layers[i % copies], xs[i % n_x], toks[i % n_x], out, ws, evs)
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            sums.setdefault(n, []).append(evs[j].elapsed_time(evs[j + 1]) * 1e3)
+    kern = {n: float(np.mean(v)) for n, v in sums.items()}
+    dom = max(kern, key=kern.get)
+    dom_bytes = kernel_bytes(dom, cfg, base, T, touched_mean)
+    achieved = dom_bytes / (kern[dom] * 1e-6) / 1e9
+
+    sbytes = step_bytes(cfg, base, T, touched_mean)
+    rec = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": workload_text(cfg), "tokens_per_step": T, "layer_copies": copies,
+                   "timing": mode, "touched_experts_per_step": touched_mean},
+        "hbm_gbps": sbytes / (ms * 1e-3) / 1e9,
+        "step_algorithmic_bytes": sbytes,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": kern[dom]},
+        "kernels_us": kern,
+        "wall_s": wall,
+        "setup_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, layer, xs_host, toks_host, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

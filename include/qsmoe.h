@@ -1,0 +1,233 @@
+/*
+ * qsmoe.h -- C ABI of the MI355X (gfx950) routed-expert MoE layer library.
+ *
+ * The layer is the DeepSeek-V4 MoE FFN as the following pages describe it
+ * (cited by page title and section):
+ *   [PR1192] mlx-lm pull request "Add DeepSeek-v4 (Flash/Pro)"
+ *   [CARD4]  model card "mlx-community / DeepSeek-V4-Flash-4bit"
+ *   [ALPHA]  model card "DeepSeek-V4-Flash-MLX-4bit"
+ *   [PR1190] mlx-lm pull request "Add DeepSeek-V4 model and safetensors/tokenizer
+ *            fallback handling"
+ *   [SERVE]  model card "DeepSeek-V4-Flash-0731-MLX-Serve-mixed-2-3-8bit"
+ *
+ *   1. route    -- fp32 gate logits, sqrtsoftplus scores, per-expert bias,
+ *                  top-k (or the tid2eid hash table), renormalised weights;
+ *   2. permute  -- bucket the T*k (token, slot) assignments by expert;
+ *   3. experts  -- per assignment, SwiGLU over group-quantised gate/up/down
+ *                  projections (affine b-bit or MXFP4), plus the shared expert;
+ *   4. combine  -- weighted sum of the k expert outputs (+ shared) per token.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates or frees device memory; all scratch comes from the
+ *    caller's workspace `ws` (size from moe_workspace_size or the per-call
+ *    sizes below). Descriptor structs are host memory, read during the call.
+ *  - Every call only enqueues work on `stream` and returns: no host sync, no
+ *    host readback of routing. Weights and inputs must stay valid until the
+ *    enqueued work completes.
+ *  - Host validation happens before anything is enqueued; a negative status
+ *    means nothing was launched. T == 0 returns MOE_OK with no launch.
+ *  - Device-side precondition violations (a token id outside [0, vocab), a
+ *    tid2eid entry or a top-k id outside [0, E)) OR a code into the sticky
+ *    error word at the start of `ws`; the offending id is replaced by 0 (and
+ *    a hash-routed token's weights by 0) so that every access stays in
+ *    bounds. Read it with moe_device_error, clear it with moe_workspace_init.
+ *  - Layouts are row-major. A quantised projection is [rows = out][cols = in]
+ *    per expert, codes packed along cols (the contraction dimension).
+ *  - bf16 arrays are passed as uint16_t bit patterns.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef QSMOE_H
+#define QSMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, k > E, ...            */
+  MOE_ERR_UNSUPPORTED = -2, /* a format/bits/group/shape the kernels lack      */
+  MOE_ERR_ALIGNMENT = -3,   /* a pointer not 16-byte aligned                   */
+  MOE_ERR_WORKSPACE = -4,   /* workspace null or smaller than required         */
+  MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed             */
+} moe_status;
+
+typedef enum { MOE_FMT_AFFINE = 0, MOE_FMT_MXFP4 = 1 } moe_format;
+typedef enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_HASH = 1 } moe_route_mode;
+typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
+
+/* Device error bits ORed into the workspace's error word. */
+#define MOE_DEVERR_TOKEN_ID 1  /* token id outside [0, vocab)                  */
+#define MOE_DEVERR_HASH_ID 2   /* tid2eid entry outside [0, E)                  */
+#define MOE_DEVERR_EXPERT_ID 4 /* top-k id passed to moe_permute outside [0, E) */
+
+/*
+ * One stacked quantised projection: num_experts matrices of [rows][cols].
+ *
+ * MOE_FMT_AFFINE ([PR1192] pre-stacked expert patch: {weight, scales, biases}
+ * triplets; [SERVE]: packs byte-compatible with MLX's affine layout; bit
+ * widths and groups from [CARD4] "Conversion" and the [SERVE] precision
+ * table): element (e, r, c) has the unsigned code q = bits [c*b, c*b + b) of
+ * row (e, r)'s LSB-first bit stream over little-endian uint32 words (a 3-bit
+ * code may straddle two words), and the value
+ *     w = scale[e][r][c / g] * q + bias[e][r][c / g]
+ * with fp16 scale and bias.  bits in {2, 3, 4, 8}, g in {32, 64, 128}.
+ *   codes  : uint32 [E][rows][cols * bits / 32]
+ *   scales : fp16   [E][rows][cols / g]
+ *   biases : fp16   [E][rows][cols / g]
+ *
+ * MOE_FMT_MXFP4 ([PR1192] mxfp4 dequantize with group_size 32, bits 4;
+ * [ALPHA]: FP4 e2m1 packed two per byte; [PR1190]: e8m0 = 2^(b - 127)):
+ * byte j of a row holds element 2j in its low nibble and 2j+1 in its high
+ * nibble; nibble n decodes to (-1)^(n >> 3) * {0, .5, 1, 1.5, 2, 3, 4, 6}[n & 7]
+ * (OCP MX e2m1), times 2^(s - 127) for the row's scale byte s of that group of
+ * 32 (s = 255 is NaN).  bits = 4, g = 32.
+ *   codes  : uint32 [E][rows][cols / 8]
+ *   scales : uint8  [E][rows][cols / 32]
+ *   biases : NULL
+ *
+ * Requirements: cols % 32 == 0, cols % g == 0, cols <= 8192, rows >= 1;
+ * codes 16-byte aligned, scales/biases 4-byte aligned.
+ */
+typedef struct {
+  int32_t format;      /* moe_format                         */
+  int32_t bits;
+  int32_t group_size;
+  int32_t rows;        /* output features                    */
+  int32_t cols;        /* input features (contraction)       */
+  int32_t num_experts;
+  const uint32_t* codes;
+  const void* scales;
+  const void* biases;
+} moe_qtensor;
+
+/* SwiGLU expert weights: gate = w1 [I][d], up = w3 [I][d], down = w2 [d][I]
+ * ([PR1192] pre-stacked rename: w1 -> gate_proj, w2 -> down_proj,
+ * w3 -> up_proj). y = W2 (silu(W1 x) * (W3 x)), with the product rounded to
+ * bf16 (round to nearest even) before the down projection. gate and up share
+ * format, bits and group; down may differ ([SERVE] precision table: gate/up
+ * 2-bit g128 with down 3-bit g128). */
+typedef struct {
+  moe_qtensor gate, up, down;
+} moe_experts;
+
+/*
+ * Router.
+ *  MOE_ROUTE_TOPK: l[t][e] = sum_i x[t][i] * weight[e][i] in fp32 ([PR1192]
+ *    cross-reference table, row "MoE gate dtype"); s = sqrt(softplus(l))
+ *    ([CARD4] "Architecture"), evaluated as sqrt(max(l,0) + log1p(exp(-|l|)))
+ *    (the logaddexp form of [PR1192]'s review notes); key = s + bias[e]; the
+ *    top_k experts by key descending, ties to the lower expert index, in that
+ *    order; weights w_j = routed_scale * s_j / sum_j s_j (the bias ranks only;
+ *    [ALPHA] "REAP-pruned builds": the router renormalises over the selected
+ *    experts).
+ *  MOE_ROUTE_HASH: ids[t][j] = tid2eid[token_ids[t]][j] in table order
+ *    ([CARD4] "Architecture": deterministic tid2eid table for the first
+ *    layers; [ALPHA]: tid2eid[vocab, 6]); weights as above from those experts'
+ *    fp32 logits; no bias.
+ *  weight : fp32 [E][hidden]; bias : fp32 [E] or NULL; tid2eid : int32
+ *  [vocab][top_k] (hash mode only). 1 <= top_k <= min(E, 8), E <= 1024,
+ *  hidden % 8 == 0.
+ */
+typedef struct {
+  int32_t mode;        /* moe_route_mode */
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t hidden;
+  int32_t vocab;       /* hash mode */
+  const float* weight;
+  const float* bias;
+  const int32_t* tid2eid;
+  float routed_scale;  /* 1.0f for the layers here */
+} moe_router;
+
+/* A whole layer. `shared` (nullable) is the always-on shared expert, added to
+ * every token with weight 1 after the routed sum ([ALPHA] "Why mixed-4_8bit"
+ * and the [SERVE] precision table name the shared experts). routed.*.num_experts
+ * must equal router.num_experts; shared->*.num_experts must be 1. */
+typedef struct {
+  moe_router router;
+  moe_experts routed;
+  const moe_experts* shared;
+} moe_layer;
+
+/* Bytes of workspace moe_forward needs for up to max_tokens tokens (0 on an
+ * invalid layer). The same size serves every other entry point. */
+size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens);
+
+/* Clear the workspace's device error word (a small kernel; capturable). */
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 1. x_bf16 [T][hidden]; token_ids int32 [T] (hash mode, else may be
+ * NULL); outputs topk_ids int32 [T][top_k], topk_w fp32 [T][top_k]. ws needs
+ * 256 + 4*T*E bytes (top-k mode logits). */
+moe_status moe_route(const moe_router* router, const uint16_t* x_bf16, const int32_t* token_ids,
+                     int32_t T, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* Step 2. A stable counting sort of the T*k assignments a = t*k + j by
+ * expert topk_ids[a]: expert_offsets int32 [E+1] (exclusive prefix sum of the
+ * per-expert counts; offsets[E] = T*k), perm int32 [T*k] (assignment indices
+ * bucketed by expert, ascending within a bucket). ws needs 256 bytes. */
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
+                       int32_t* expert_offsets, int32_t* perm, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Step 3. For each bucketed assignment a (token t = a / k) of expert e:
+ * y_slot[a] = expert_e(x[t]) in fp32, written in assignment order a, so row
+ * t*k + j is token t's j-th expert. If `shared` is non-NULL, y_shared[t] =
+ * shared(x[t]) for every token (y_shared may be NULL only when shared is).
+ * y_slot fp32 [T*k][hidden], y_shared fp32 [T][hidden]. ws: see
+ * moe_workspace_size. */
+moe_status moe_expert_ffn(const moe_experts* routed, const moe_experts* shared,
+                          const uint16_t* x_bf16, int32_t T, int32_t k,
+                          const int32_t* expert_offsets, const int32_t* perm, float* y_slot,
+                          float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Step 4. out[t] = sum_{j=0..k-1} topk_w[t][j] * y_slot[t*k + j] (j in
+ * order) + y_shared[t] (if non-NULL), accumulated in fp32; stored as bf16
+ * (round to nearest even) or fp32 per out_dtype. d % 4 == 0. */
+moe_status moe_combine(const float* y_slot, const float* topk_w, const float* y_shared, int32_t T,
+                       int32_t k, int32_t d, int32_t out_dtype, void* out, hipStream_t stream);
+
+/* Steps 1-4 in one call: out [T][hidden] (bf16 or fp32). token_ids is needed
+ * in hash mode only. ws >= moe_workspace_size(layer, T). */
+moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids,
+                       int32_t T, int32_t out_dtype, void* out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Test and inspection helpers (not on the hot path). */
+
+/* Router logits only: logits fp32 [T][E] (top-k mode's first kernel). */
+moe_status moe_router_logits(const moe_router* router, const uint16_t* x_bf16, int32_t T,
+                             float* logits, hipStream_t stream);
+
+/* moe_forward with timing probes: records events[0] on `stream` before the
+ * first kernel and events[i] after the i-th kernel, and stores the kernels'
+ * names (static strings) in names[i-1] and their count in *n_kernels.
+ * n_events must exceed the number of kernels (at most 16 are launched). The
+ * caller creates the events. Same results as moe_forward. */
+moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids,
+                              int32_t T, int32_t out_dtype, void* out, void* ws, size_t ws_bytes,
+                              hipStream_t stream, hipEvent_t* events, int32_t n_events, const char** names,
+                              int32_t* n_kernels);
+
+/* Synchronises `stream`, then copies the workspace error word to *code_out. */
+moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream);
+
+const char* moe_status_string(moe_status status);
+
+/* Library version string. */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSMOE_H */

@@ -1,0 +1,360 @@
+// C ABI of the MoE layer library: host validation, workspace carving and the
+// launch sequence. Nothing here allocates device memory or synchronises,
+// except moe_device_error, which exists for tests.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/qsmoe.h"
+#include "kernels.hpp"
+
+using namespace qsmoe;
+
+namespace {
+
+constexpr size_t kHeader = 256;  // error word + padding at the start of every workspace
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int ilog2(int v) {
+  int r = 0;
+  while ((1 << r) < v) ++r;
+  return r;
+}
+
+moe_status check_qtensor(const moe_qtensor& q, int experts, int rows, int cols) {
+  if (q.codes == nullptr || q.scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (q.rows != rows || q.cols != cols || q.num_experts != experts || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARG;
+  if (q.format == MOE_FMT_AFFINE) {
+    if (q.biases == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!(q.bits == 2 || q.bits == 3 || q.bits == 4 || q.bits == 8)) return MOE_ERR_UNSUPPORTED;
+    if (!(q.group_size == 32 || q.group_size == 64 || q.group_size == 128)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned(q.scales, 2) || !aligned(q.biases, 2)) return MOE_ERR_ALIGNMENT;
+  } else if (q.format == MOE_FMT_MXFP4) {
+    if (q.bits != 4 || q.group_size != 32) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (cols % 32 != 0 || cols % q.group_size != 0 || cols > 8192) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(q.codes, 16)) return MOE_ERR_ALIGNMENT;
+  return MOE_OK;
+}
+
+QMat to_qmat(const moe_qtensor& q) {
+  QMat m;
+  m.codes = q.codes;
+  m.scales = q.scales;
+  m.biases = static_cast<const uint16_t*>(q.format == MOE_FMT_AFFINE ? q.biases : nullptr);
+  m.fmt = q.format;
+  m.bits = q.bits;
+  m.group = q.group_size;
+  m.rows = q.rows;
+  m.cols = q.cols;
+  m.row_words = q.cols * q.bits / 32;
+  m.row_groups = q.cols / q.group_size;
+  m.gshift = ilog2(q.group_size / 32);
+  return m;
+}
+
+// Shape of an expert set: d = gate.cols, I = gate.rows.
+moe_status check_experts(const moe_experts& x, int experts, int d_expected) {
+  const int d = x.gate.cols, I = x.gate.rows;
+  if (d_expected > 0 && d != d_expected) return MOE_ERR_INVALID_ARG;
+  moe_status s;
+  if ((s = check_qtensor(x.gate, experts, I, d)) != MOE_OK) return s;
+  if ((s = check_qtensor(x.up, experts, I, d)) != MOE_OK) return s;
+  if ((s = check_qtensor(x.down, experts, d, I)) != MOE_OK) return s;
+  if (x.up.format != x.gate.format || x.up.bits != x.gate.bits || x.up.group_size != x.gate.group_size)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_router(const moe_router& r) {
+  if (r.weight == nullptr) return MOE_ERR_INVALID_ARG;
+  if (r.num_experts < 1 || r.num_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (r.top_k < 1 || r.top_k > r.num_experts || r.top_k > 8) return MOE_ERR_INVALID_ARG;
+  if (r.hidden < 8 || r.hidden % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(r.weight, 16)) return MOE_ERR_ALIGNMENT;
+  if (r.bias != nullptr && !aligned(r.bias, 4)) return MOE_ERR_ALIGNMENT;
+  if (r.mode == MOE_ROUTE_HASH) {
+    if (r.tid2eid == nullptr || r.vocab < 1) return MOE_ERR_INVALID_ARG;
+    if (!aligned(r.tid2eid, 4)) return MOE_ERR_ALIGNMENT;
+  } else if (r.mode != MOE_ROUTE_TOPK) {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer* L) {
+  if (L == nullptr) return MOE_ERR_INVALID_ARG;
+  moe_status s;
+  if ((s = check_router(L->router)) != MOE_OK) return s;
+  if ((s = check_experts(L->routed, L->router.num_experts, L->router.hidden)) != MOE_OK) return s;
+  if (L->shared && (s = check_experts(*L->shared, 1, L->router.hidden)) != MOE_OK) return s;
+  return MOE_OK;
+}
+
+size_t route_ws_bytes(const moe_router& r, int T) {
+  return kHeader + (r.mode == MOE_ROUTE_TOPK ? align_up(static_cast<size_t>(T) * r.num_experts * 4) : 0);
+}
+
+size_t ffn_ws_bytes(const moe_experts& routed, const moe_experts* shared, int T, int k) {
+  size_t b = kHeader + align_up(static_cast<size_t>(T) * k * routed.gate.rows * 2);
+  if (shared) b += align_up(static_cast<size_t>(T) * shared->gate.rows * 2);
+  return b;
+}
+
+struct FwdLayout {
+  size_t ids, w, logits, offsets, perm, h, h_sh, y_slot, y_sh, total;
+};
+
+FwdLayout forward_layout(const moe_layer& L, int T) {
+  const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;
+  const size_t tk = static_cast<size_t>(T) * k;
+  FwdLayout f;
+  size_t o = kHeader;
+  f.ids = o;
+  o += align_up(tk * 4);
+  f.w = o;
+  o += align_up(tk * 4);
+  f.logits = o;
+  o += L.router.mode == MOE_ROUTE_TOPK ? align_up(static_cast<size_t>(T) * E * 4) : 0;
+  f.offsets = o;
+  o += align_up((E + 1) * 4);
+  f.perm = o;
+  o += align_up(tk * 4);
+  f.h = o;
+  o += align_up(tk * L.routed.gate.rows * 2);
+  f.h_sh = o;
+  o += L.shared ? align_up(static_cast<size_t>(T) * L.shared->gate.rows * 2) : 0;
+  f.y_slot = o;
+  o += align_up(tk * d * 4);
+  f.y_sh = o;
+  o += L.shared ? align_up(static_cast<size_t>(T) * d * 4) : 0;
+  f.total = o;
+  return f;
+}
+
+// Optional timing probe of moe_forward_probed: an event after every launch.
+struct Probe {
+  hipEvent_t* events;
+  int32_t n_events;
+  const char** names;
+  int32_t count;
+  bool overflow;
+};
+thread_local Probe* g_probe = nullptr;
+
+hipError_t mark(hipError_t launched, const char* name, hipStream_t s) {
+  if (launched != hipSuccess || g_probe == nullptr) return launched;
+  Probe& p = *g_probe;
+  if (p.count + 1 >= p.n_events) {
+    p.overflow = true;
+    return launched;
+  }
+  p.names[p.count] = name;
+  p.count += 1;
+  return hipEventRecord(p.events[p.count], s);
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(static_cast<char*>(ws) + off);
+}
+
+moe_status run_route(const moe_router& r, const uint16_t* x, const int32_t* token_ids, int T, int32_t* ids,
+                     float* w, float* logits, int32_t* err, hipStream_t s) {
+  hipError_t e;
+  if (r.mode == MOE_ROUTE_HASH) {
+    e = mark(launch_router_hash(x, r.weight, token_ids, r.tid2eid, T, r.num_experts, r.top_k, r.hidden, r.vocab,
+                                r.routed_scale, ids, w, err, s),
+             "router_hash", s);
+    return hip_status(e);
+  }
+  if ((e = mark(launch_router_logits(x, r.weight, T, r.num_experts, r.hidden, logits, s), "router_logits", s)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return hip_status(
+      mark(launch_router_topk(logits, r.bias, T, r.num_experts, r.top_k, r.routed_scale, ids, w, s), "router_topk", s));
+}
+
+moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const uint16_t* x, int T, int k, int E,
+                   const int32_t* offsets, const int32_t* perm, float* y_slot, float* y_sh, uint16_t* h,
+                   uint16_t* h_sh, hipStream_t s) {
+  if (shared) {
+    GateUpArgs g{to_qmat(shared->gate), to_qmat(shared->up), x, T, k, 1, nullptr, nullptr, 1, h_sh};
+    if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  GateUpArgs g{to_qmat(routed.gate), to_qmat(routed.up), x, T, k, E, offsets, perm, 0, h};
+  if (mark(launch_gateup(g, s), "routed_gateup", s) != hipSuccess) return MOE_ERR_HIP;
+  if (shared) {
+    DownArgs dn{to_qmat(shared->down), h_sh, T, k, 1, nullptr, nullptr, 1, y_sh};
+    if (mark(launch_down(dn, s), "shared_down", s) != hipSuccess) return MOE_ERR_HIP;
+  }
+  DownArgs dn{to_qmat(routed.down), h, T, k, E, offsets, perm, 0, y_slot};
+  return hip_status(mark(launch_down(dn, s), "routed_down", s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_version(void) { return "qsmoe 0.1.0 (gfx950)"; }
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case MOE_ERR_ALIGNMENT: return "misaligned pointer";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens) {
+  if (max_tokens < 0 || check_layer(layer) != MOE_OK) return 0;
+  return forward_layout(*layer, max_tokens > 0 ? max_tokens : 1).total;
+}
+
+moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (ws == nullptr || ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_fill_i32(static_cast<int32_t*>(ws), 0, 1, stream));
+}
+
+moe_status moe_router_logits(const moe_router* router, const uint16_t* x_bf16, int32_t T, float* logits,
+                             hipStream_t stream) {
+  if (router == nullptr || x_bf16 == nullptr || logits == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_router(*router);
+  if (s != MOE_OK) return s;
+  if (!aligned(x_bf16, 16)) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_router_logits(x_bf16, router->weight, T, router->num_experts, router->hidden, logits,
+                                         stream));
+}
+
+moe_status moe_route(const moe_router* router, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                     int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (router == nullptr || x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr || T < 0)
+    return MOE_ERR_INVALID_ARG;
+  moe_status s = check_router(*router);
+  if (s != MOE_OK) return s;
+  if (router->mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16)) return MOE_ERR_ALIGNMENT;
+  if (ws == nullptr || ws_bytes < route_ws_bytes(*router, T)) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  return run_route(*router, x_bf16, token_ids, T, topk_ids, topk_w, at<float>(ws, kHeader), at<int32_t>(ws, 0),
+                   stream);
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,
+                       int32_t* perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (topk_ids == nullptr || expert_offsets == nullptr || perm == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (k < 1 || k > E || k > 8) return MOE_ERR_INVALID_ARG;
+  if (ws == nullptr || ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_permute(topk_ids, T * k, E, expert_offsets, perm, at<int32_t>(ws, 0), stream));
+}
+
+moe_status moe_expert_ffn(const moe_experts* routed, const moe_experts* shared, const uint16_t* x_bf16, int32_t T,
+                          int32_t k, const int32_t* expert_offsets, const int32_t* perm, float* y_slot,
+                          float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (routed == nullptr || x_bf16 == nullptr || expert_offsets == nullptr || perm == nullptr || y_slot == nullptr ||
+      T < 0)
+    return MOE_ERR_INVALID_ARG;
+  const int E = routed->gate.num_experts;
+  moe_status s = check_experts(*routed, E, 0);
+  if (s != MOE_OK) return s;
+  if (E < 1 || E > 1024) return MOE_ERR_UNSUPPORTED;
+  if (k < 1 || k > E || k > 8) return MOE_ERR_INVALID_ARG;
+  if (shared) {
+    if ((s = check_experts(*shared, 1, routed->gate.cols)) != MOE_OK) return s;
+    if (y_shared == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned(y_shared, 16)) return MOE_ERR_ALIGNMENT;
+  }
+  if (!aligned(x_bf16, 16) || !aligned(y_slot, 16)) return MOE_ERR_ALIGNMENT;
+  if (ws == nullptr || ws_bytes < ffn_ws_bytes(*routed, shared, T, k)) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  uint16_t* h = at<uint16_t>(ws, kHeader);
+  uint16_t* h_sh = at<uint16_t>(ws, kHeader + align_up(static_cast<size_t>(T) * k * routed->gate.rows * 2));
+  return run_ffn(*routed, shared, x_bf16, T, k, E, expert_offsets, perm, y_slot, y_shared, h, h_sh, stream);
+}
+
+moe_status moe_combine(const float* y_slot, const float* topk_w, const float* y_shared, int32_t T, int32_t k,
+                       int32_t d, int32_t out_dtype, void* out, hipStream_t stream) {
+  if (y_slot == nullptr || topk_w == nullptr || out == nullptr || T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARG;
+  if (d % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!aligned(y_slot, 16) || !aligned(out, 8) || (y_shared && !aligned(y_shared, 16))) return MOE_ERR_ALIGNMENT;
+  if (out_dtype == MOE_OUT_F32 && !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  return hip_status(launch_combine(y_slot, topk_w, y_shared, T, k, d, out_dtype == MOE_OUT_F32, out, stream));
+}
+
+moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                       int32_t out_dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (x_bf16 == nullptr || out == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_layer(layer);
+  if (s != MOE_OK) return s;
+  const moe_layer& L = *layer;
+  if (L.router.mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
+  if (ws == nullptr) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  if (T == 0) return MOE_OK;
+  const FwdLayout f = forward_layout(L, T);
+  if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
+  const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;
+  int32_t* err = at<int32_t>(ws, 0);
+  int32_t* ids = at<int32_t>(ws, f.ids);
+  float* w = at<float>(ws, f.w);
+  int32_t* offsets = at<int32_t>(ws, f.offsets);
+  int32_t* perm = at<int32_t>(ws, f.perm);
+  float* y_slot = at<float>(ws, f.y_slot);
+  float* y_sh = L.shared ? at<float>(ws, f.y_sh) : nullptr;
+  if ((s = run_route(L.router, x_bf16, token_ids, T, ids, w, at<float>(ws, f.logits), err, stream)) != MOE_OK)
+    return s;
+  if (mark(launch_permute(ids, T * k, E, offsets, perm, err, stream), "permute", stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if ((s = run_ffn(L.routed, L.shared, x_bf16, T, k, E, offsets, perm, y_slot, y_sh, at<uint16_t>(ws, f.h),
+                   at<uint16_t>(ws, f.h_sh), stream)) != MOE_OK)
+    return s;
+  return hip_status(
+      mark(launch_combine(y_slot, w, y_sh, T, k, d, out_dtype == MOE_OUT_F32, out, stream), "combine", stream));
+}
+
+moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                              int32_t out_dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t* events, int32_t n_events, const char** names, int32_t* n_kernels) {
+  if (events == nullptr || names == nullptr || n_kernels == nullptr || n_events < 2) return MOE_ERR_INVALID_ARG;
+  Probe p{events, n_events, names, 0, false};
+  *n_kernels = 0;
+  if (T > 0 && hipEventRecord(events[0], stream) != hipSuccess) return MOE_ERR_HIP;
+  g_probe = &p;
+  const moe_status s = moe_forward(layer, x_bf16, token_ids, T, out_dtype, out, ws, ws_bytes, stream);
+  g_probe = nullptr;
+  *n_kernels = p.count;
+  if (s == MOE_OK && p.overflow) return MOE_ERR_INVALID_ARG;
+  return s;
+}
+
+moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream) {
+  if (ws == nullptr || code_out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(hipMemcpy(code_out, ws, sizeof(int32_t), hipMemcpyDeviceToHost));
+}
+
+}  // extern "C"

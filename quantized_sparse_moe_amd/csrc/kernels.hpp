@@ -1,0 +1,73 @@
+// Internal launch interface between the C ABI (host.hip) and the kernel
+// translation units. Everything here is already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsmoe {
+
+// One stacked quantised projection as the kernels see it.
+struct QMat {
+  const uint32_t* codes;  // [n][rows][row_words]
+  const void* scales;     // fp16 (affine) or uint8 e8m0 (mxfp4), [n][rows][row_groups]
+  const uint16_t* biases; // fp16 (affine) or null
+  int32_t fmt;            // 0 affine, 1 mxfp4
+  int32_t bits;
+  int32_t group;
+  int32_t rows;
+  int32_t cols;
+  int32_t row_words;      // cols * bits / 32
+  int32_t row_groups;     // cols / group
+  int32_t gshift;         // log2(group / 32)
+};
+
+// Router ---------------------------------------------------------------------
+hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E, int d, float* logits,
+                                hipStream_t s);
+hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k, float routed_scale,
+                              int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_router_hash(const uint16_t* x, const float* wr, const int32_t* token_ids,
+                              const int32_t* tid2eid, int T, int E, int k, int d, int vocab, float routed_scale,
+                              int32_t* ids, float* w, int32_t* err, hipStream_t s);
+
+// Bucketing ------------------------------------------------------------------
+hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* perm, int32_t* err,
+                          hipStream_t s);
+
+// Experts (GEMV path: few tokens per expert) ---------------------------------
+// Routed mode: expert_offsets/perm given, n_buckets = min(T*k, E).
+// Shared mode: one expert, bucket b covers tokens [b*NT, b*NT + NT).
+struct GateUpArgs {
+  QMat gate, up;           // rows = I, cols = d
+  const uint16_t* x;       // bf16 [T][d]
+  int32_t T, k, E;
+  const int32_t* offsets;  // routed only
+  const int32_t* perm;     // routed only
+  int32_t shared;
+  uint16_t* h;             // bf16 [T*k][I] in bucketed order (routed) or [T][I] (shared)
+};
+hipError_t launch_gateup(const GateUpArgs& a, hipStream_t s);
+
+struct DownArgs {
+  QMat down;               // rows = d, cols = I
+  const uint16_t* h;       // bf16, as written by launch_gateup
+  int32_t T, k, E;
+  const int32_t* offsets;
+  const int32_t* perm;
+  int32_t shared;
+  float* y;                // fp32 [T*k][d] in assignment order (routed) or [T][d] (shared)
+};
+hipError_t launch_down(const DownArgs& a, hipStream_t s);
+
+// Combine --------------------------------------------------------------------
+hipError_t launch_combine(const float* y_slot, const float* w, const float* y_shared, int T, int k, int d,
+                          int out_f32, void* out, hipStream_t s);
+
+// Workspace ------------------------------------------------------------------
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
+
+// Does a GEMV kernel exist for this projection shape/format?
+bool gemv_supported(const QMat& m);
+
+}  // namespace qsmoe

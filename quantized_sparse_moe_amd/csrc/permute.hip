@@ -1,0 +1,121 @@
+// Bucketing of the T*k (token, slot) assignments by expert: a stable counting
+// sort in one workgroup of 8 waves.
+//
+// The stacked expert tensors (mlx-lm PR "Add DeepSeek-v4 (Flash/Pro)",
+// pre-stacked switch_mlp.{gate,up,down}_proj) are run over contiguous buckets
+// of assignments, so each expert's weights are streamed once per step.
+//
+// Wave w owns a contiguous segment of assignments. Lanes holding the same
+// expert id are grouped with one ballot per id bit (no atomics); the group's
+// lowest lane is its leader. Pass 1 counts per (wave, expert) in LDS; a scan
+// over (expert, wave) gives every wave its base per expert; pass 2 writes
+// perm[base + rank-within-group] and advances the base. Order within a bucket
+// is ascending assignment index, i.e. the sort is stable.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qsmoe {
+
+constexpr int kPermWaves = 8;
+
+__device__ __forceinline__ uint64_t same_id_mask(bool valid, int id, int nbits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (id >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kPermWaves * 64) void k_permute(const int32_t* __restrict__ ids, int n, int E,
+                                                             int nbits, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ perm, int32_t* err) {
+  extern __shared__ int32_t lds[];
+  int32_t* hist = lds;                        // [kPermWaves][E]
+  int32_t* wave_tot = lds + kPermWaves * E;   // [kPermWaves] scan scratch
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int nthreads = kPermWaves * 64;
+  for (int i = tid; i < kPermWaves * E; i += nthreads) hist[i] = 0;
+  __syncthreads();
+
+  const int seg = ((n + kPermWaves - 1) / kPermWaves + 63) & ~63;
+  const int s0 = min(n, w * seg), s1 = min(n, s0 + seg);
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+
+  // pass 1: per-wave histogram
+  for (int base = s0; base < s1; base += 64) {
+    const int a = base + lane;
+    const bool valid = a < s1;
+    int id = valid ? ids[a] : 0;
+    if (valid && (id < 0 || id >= E)) {
+      set_device_error(err, 4);
+      id = 0;
+    }
+    const uint64_t m = same_id_mask(valid, id, nbits);
+    if (valid && (m & lt_mask) == 0) hist[w * E + id] += __popcll(m);
+  }
+  __syncthreads();
+
+  // per-expert totals, exclusive scan over experts, per-wave bases
+  int carry = 0;
+  for (int e0 = 0; e0 < E; e0 += nthreads) {
+    const int e = e0 + tid;
+    int tot = 0;
+    if (e < E)
+      for (int v = 0; v < kPermWaves; ++v) tot += hist[v * E + e];
+    // inclusive wave scan
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    int wave_base = 0, chunk_total = 0;
+    for (int v = 0; v < kPermWaves; ++v) {
+      if (v < w) wave_base += wave_tot[v];
+      chunk_total += wave_tot[v];
+    }
+    const int excl = carry + wave_base + incl - tot;
+    if (e < E) {
+      offsets[e] = excl;
+      int run = excl;
+      for (int v = 0; v < kPermWaves; ++v) {
+        const int c = hist[v * E + e];
+        hist[v * E + e] = run;
+        run += c;
+      }
+    }
+    carry += chunk_total;
+    __syncthreads();
+  }
+  if (tid == 0) offsets[E] = n;
+  __syncthreads();
+
+  // pass 2: stable scatter
+  for (int base = s0; base < s1; base += 64) {
+    const int a = base + lane;
+    const bool valid = a < s1;
+    int id = valid ? ids[a] : 0;
+    if (id < 0 || id >= E) id = 0;
+    const uint64_t m = same_id_mask(valid, id, nbits);
+    if (valid) {
+      const int pos = hist[w * E + id] + __popcll(m & lt_mask);
+      perm[pos] = a;
+    }
+    if (valid && (m & lt_mask) == 0) hist[w * E + id] += __popcll(m);
+  }
+}
+
+hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* offsets, int32_t* perm, int32_t* err,
+                          hipStream_t s) {
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const size_t lds = (static_cast<size_t>(kPermWaves) * E + kPermWaves) * sizeof(int32_t);
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermWaves * 64), lds, s, ids, n, E, nbits, offsets, perm, err);
+  return hipGetLastError();
+}
+
+}  // namespace qsmoe

@@ -1,0 +1,140 @@
+"""Edge cases on the GPU: k = E, a single expert, duplicate hash-table ids,
+zero weights, zero tokens, device error words for out-of-range ids (forced
+from the host with in-bounds fallbacks), and determinism with a poisoned
+workspace."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_sparse_moe_amd as qm
+import synth
+from quantized_sparse_moe_amd import _lib
+from synth import variant
+from tests._gpu import TOL, rel_err, run_staged, stable_sort_perm, xdev
+
+pytestmark = pytest.mark.gpu
+
+
+def _parity(cfg, layer, x, tok=None):
+    dl = qm.DeviceLayer.from_host(layer)
+    st, out, _, _ = run_staged(dl, x, tok)
+    ref = oracle.forward(layer, x, token_ids=tok)
+    assert np.array_equal(st.ids.cpu().numpy(), ref.ids)
+    assert rel_err(out.cpu().numpy(), ref.y).max() <= TOL
+    return st, ref
+
+
+def test_k_equals_E():
+    cfg = variant("tiny", "kE", 201, E=8, top_k=8, T=5)
+    layer = synth.gen_layer(cfg)
+    st, _ = _parity(cfg, layer, synth.gen_x(cfg, 0))
+    assert np.all(np.sort(st.ids.cpu().numpy(), 1) == np.arange(8))
+
+
+def test_single_expert():
+    cfg = variant("tiny", "E1", 202, E=1, top_k=1, T=6)
+    layer = synth.gen_layer(cfg)
+    st, _ = _parity(cfg, layer, synth.gen_x(cfg, 0))
+    assert np.all(st.w.cpu().numpy() == 1.0)
+
+
+def test_hash_duplicate_ids_are_separate_slots():
+    cfg = variant("hash", "dup", 203, T=12, d=256, I=128, E=8, top_k=3, vocab=10)
+    layer = synth.gen_layer(cfg)
+    layer.tid2eid[:] = np.array([[1, 1, 5]] * 10, np.int32)
+    layer.tid2eid[3] = [7, 7, 7]
+    x = synth.gen_x(cfg, 0)
+    tok = synth.gen_token_ids(cfg, 0)
+    tok[0] = 3
+    _parity(cfg, layer, x, tok)
+
+
+def test_zero_weights_give_zero_output():
+    cfg = variant("mixed", "zero", 204, T=4, d=256, I=128, E=8, top_k=2, I_shared=128)
+    layer = synth.gen_layer(cfg)
+    for ew in (layer.routed, layer.shared):
+        for q in (ew.gate, ew.up, ew.down):
+            q.scales[:] = 0
+            q.biases[:] = 0
+    dl = qm.DeviceLayer.from_host(layer)
+    out = qm.forward(dl, xdev(synth.gen_x(cfg, 0)), out_dtype="f32")
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_zero_tokens_launches_nothing():
+    cfg = synth.config("tiny")
+    dl = qm.DeviceLayer.from_host(synth.gen_layer(cfg))
+    x = torch.empty((0, cfg.d), dtype=torch.int16, device="cuda")
+    out = qm.forward(dl, x, out_dtype="f32", ws=dl.workspace(1))
+    assert out.shape == (0, cfg.d)
+
+
+def test_out_of_range_token_id_sets_error_word():
+    cfg = variant("hash", "badtok", 205, T=8, d=256, I=128, E=16, top_k=2, vocab=50)
+    layer = synth.gen_layer(cfg)
+    dl = qm.DeviceLayer.from_host(layer)
+    x = synth.gen_x(cfg, 0)
+    tok = synth.gen_token_ids(cfg, 0)
+    good = tok.copy()
+    tok[3] = 50
+    ws = dl.workspace(cfg.T)
+    out = qm.forward(dl, xdev(x), torch.from_numpy(tok).cuda(), out_dtype="f32", ws=ws)
+    assert qm.device_error(ws) & _lib.MOE_DEVERR_TOKEN_ID
+    ref = oracle.forward(layer, x, token_ids=good)
+    keep = [t for t in range(cfg.T) if t != 3]
+    assert rel_err(out.cpu().numpy()[keep], ref.y[keep]).max() <= TOL
+    assert torch.count_nonzero(out[3]).item() == 0
+    qm.workspace_init(ws)
+    assert qm.device_error(ws) == 0
+
+
+def test_out_of_range_table_entry_sets_error_word():
+    cfg = variant("hash", "badtab", 206, T=4, d=256, I=128, E=16, top_k=2, vocab=20)
+    layer = synth.gen_layer(cfg)
+    layer.tid2eid[:, 1] = 16
+    dl = qm.DeviceLayer.from_host(layer)
+    ws = dl.workspace(cfg.T)
+    tok = torch.from_numpy(synth.gen_token_ids(cfg, 0)).cuda()
+    qm.forward(dl, xdev(synth.gen_x(cfg, 0)), tok, ws=ws)
+    assert qm.device_error(ws) & _lib.MOE_DEVERR_HASH_ID
+
+
+def test_permute_flags_bad_expert_ids():
+    ids = torch.tensor([[0, 3], [9, 1], [2, -1]], dtype=torch.int32, device="cuda")
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    qm.workspace_init(ws)
+    off, perm = qm.permute(ids, 4, ws)
+    assert qm.device_error(ws) & _lib.MOE_DEVERR_EXPERT_ID
+    p = perm.cpu().numpy()
+    assert sorted(p.tolist()) == list(range(6))   # still a permutation
+    assert off.cpu().numpy()[-1] == 6
+
+
+@pytest.mark.parametrize("T,E", [(1, 256), (700, 64), (4096, 256), (1500, 1000)])
+def test_permute_large_and_wide(T, E):
+    rng = np.random.default_rng(T + E)
+    k = 6
+    ids_np = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    qm.workspace_init(ws)
+    off, perm = qm.permute(torch.from_numpy(ids_np).cuda(), E, ws)
+    o, p = stable_sort_perm(ids_np, E)
+    assert np.array_equal(off.cpu().numpy(), o) and np.array_equal(perm.cpu().numpy(), p)
+    assert qm.device_error(ws) == 0
+
+
+def test_deterministic_with_poisoned_workspace():
+    cfg = variant("mixed", "det", 207, T=16, d=512, I=256, E=32, I_shared=256)
+    layer = synth.gen_layer(cfg)
+    dl = qm.DeviceLayer.from_host(layer)
+    x = xdev(synth.gen_x(cfg, 0))
+    clean = dl.workspace(cfg.T)
+    a = qm.forward(dl, x, out_dtype="f32", ws=clean)
+    ws = torch.full((dl.workspace_size(cfg.T),), 0xFF, dtype=torch.uint8, device="cuda")
+    qm.workspace_init(ws)
+    b = qm.forward(dl, x, out_dtype="f32", ws=ws)
+    c = qm.forward(dl, x, out_dtype="f32", ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(b, c)
+    assert qm.device_error(ws) == 0

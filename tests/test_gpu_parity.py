@@ -1,0 +1,99 @@
+"""GPU parity against the float64 oracle on seeded inputs small enough for the
+oracle to finish in seconds, yet spanning several tiles, several tokens per
+expert bucket and ragged tails (hidden sizes that leave lanes idle, token
+counts that leave the last pass of a bucket partial).
+
+Bar: routing ids equal the oracle's except certified float64 near-ties;
+permutations equal the stable sort of the GPU's ids exactly; routed, shared and
+combined outputs within max relative error 2e-3 per token (fp32 output mode);
+the bf16 output is the round-to-nearest-even of the fp32 output, bit for bit;
+the one-shot forward equals the four entry points called in turn, bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_sparse_moe_amd as qm
+import synth
+from synth import FormatSpec, variant
+from tests._gpu import TOL, check_topk_ids, rel_err, run_staged, stable_sort_perm, xdev
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    synth.config("tiny"),
+    variant("decode", "decode_s", 102, T=3, d=512, I=256, E=32, I_shared=256, steps=2),
+    variant("hash", "hash_s", 103, T=40, d=512, I=256, E=32, vocab=1000),
+    variant("prefill", "prefill_s", 104, T=200, d=512, I=256, E=32),
+    variant("mixed", "mixed_s", 105, T=24, d=512, I=256, E=32, I_shared=256),
+    variant("decode", "ragged_g32", 106, T=7, d=2400, I=224, E=24, top_k=3, gate_up=FormatSpec("affine", 4, 32),
+            down=FormatSpec("affine", 4, 32), shared=FormatSpec("affine", 8, 32), I_shared=96),
+    variant("mixed", "mixed_2x8", 107, T=9, d=4096, I=256, E=16, top_k=4, gate_up=FormatSpec("affine", 8, 64),
+            down=FormatSpec("affine", 2, 64), shared=FormatSpec("affine", 3, 32), I_shared=128),
+    variant("prefill", "mxfp4_wide", 108, T=33, d=6144, I=128, E=8, top_k=2, bias_kind="normal"),
+]
+
+
+def check_layer(cfg, layer, dl, step):
+    x = synth.gen_x(cfg, step)
+    tok = synth.gen_token_ids(cfg, step)
+    st, out_f32, out_bf16, _ = run_staged(dl, x, tok)
+    ref = oracle.forward(layer, x, token_ids=tok)
+    gids = st.ids.cpu().numpy()
+    k, E = cfg.top_k, cfg.E
+    if cfg.route == "topk":
+        check_topk_ids(gids, ref.ids, ref.key, k)
+    else:
+        assert np.array_equal(gids, ref.ids)
+    off, perm = stable_sort_perm(gids, E)
+    assert np.array_equal(st.offsets.cpu().numpy(), off)
+    assert np.array_equal(st.perm.cpu().numpy(), perm)
+    if not np.array_equal(gids, ref.ids):
+        ref = oracle.forward(layer, x, token_ids=tok, ids=gids)
+    assert np.allclose(st.w.cpu().numpy(), ref.w, rtol=2e-6, atol=1e-7)
+    e_slot = rel_err(st.y_slot.cpu().numpy(), ref.y_slot)
+    assert e_slot.max() <= TOL, e_slot.max()
+    if layer.shared is not None:
+        e_sh = rel_err(st.y_shared.cpu().numpy(), ref.y_shared)
+        assert e_sh.max() <= TOL, e_sh.max()
+    e = rel_err(out_f32.cpu().numpy(), ref.y)
+    assert e.max() <= TOL, e.max()
+    assert torch.equal(st.out, out_f32)
+    assert torch.equal(out_f32.to(torch.bfloat16), out_bf16)
+    return e.max()
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small_layer_parity(cfg):
+    layer = synth.gen_layer(cfg)
+    dl = qm.DeviceLayer.from_host(layer)
+    worst = max(check_layer(cfg, layer, dl, s) for s in range(min(cfg.steps, 2)))
+    print(f"{cfg.name}: max rel err {worst:.2e}")
+
+
+def test_router_logits_and_topk_on_gpu_keys():
+    """Logits within fp32 accumulation error of float64; the GPU top-k equals
+    a host top-k over the GPU's own fp32 logits (scores in fp32), except where
+    two fp32 keys lie within a few ulps."""
+    cfg = variant("prefill", "logits", 111, T=300, d=1024, I=128, E=64)
+    wr, bias = synth.gen_router(cfg)
+    layer = synth.Layer(cfg, wr, bias, None, synth.gen_routed_stacked(cfg), None)
+    dl = qm.DeviceLayer.from_host(layer)
+    x = synth.gen_x(cfg, 0)
+    xd = xdev(x)
+    logits = qm.router_logits(dl, xd).cpu().numpy()
+    ref = oracle.router_logits(oracle.bf16_bits_to_f64(x), wr)
+    scale = np.abs(oracle.bf16_bits_to_f64(x)) @ np.abs(wr.astype(np.float64)).T
+    assert np.all(np.abs(logits - ref) <= 1e-5 * scale + 1e-30)
+    ids, w = qm.route(dl, xd)
+    ids = ids.cpu().numpy()
+    l32 = logits.astype(np.float32)
+    s32 = np.sqrt(np.maximum(l32, 0) + np.log1p(np.exp(-np.abs(l32)))).astype(np.float32)
+    key32 = (s32 + bias[None, :]).astype(np.float32)
+    for t in range(cfg.T):
+        order = sorted(range(cfg.E), key=lambda e: (-key32[t, e], e))[:cfg.top_k]
+        if ids[t].tolist() != order:
+            diff = set(order) ^ set(ids[t].tolist())
+            kth = key32[t, order[-1]]
+            assert all(abs(key32[t, e] - kth) <= 4 * np.spacing(np.abs(kth)) for e in diff) or not diff
