@@ -200,11 +200,14 @@ def main():
 
     # per-kernel durations: events between kernels, host kept ahead of the GPU
     n_ev = 17
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for e in evs:
+        e.record()  # torch creates the HIP event on first use
+    torch.cuda.synchronize()
     probe_steps = min(K, 64)
     sums = {}
     for i in range(probe_steps):
         torch.cuda._sleep(2_000_000)  # lets the host enqueue the step before it runs
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
         names = qm.forward_probed(layers[i % copies], xs[i % n_x], toks[i % n_x], out, ws, evs)
         torch.cuda.synchronize()
         for j, n in enumerate(names):

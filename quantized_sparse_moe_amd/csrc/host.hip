@@ -232,61 +232,63 @@ moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
 
 moe_status moe_router_logits(const moe_router* router, const uint16_t* x_bf16, int32_t T, float* logits,
                              hipStream_t stream) {
-  if (router == nullptr || x_bf16 == nullptr || logits == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  if (router == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
   moe_status s = check_router(*router);
   if (s != MOE_OK) return s;
-  if (!aligned(x_bf16, 16)) return MOE_ERR_ALIGNMENT;
   if (T == 0) return MOE_OK;
+  if (x_bf16 == nullptr || logits == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x_bf16, 16)) return MOE_ERR_ALIGNMENT;
   return hip_status(launch_router_logits(x_bf16, router->weight, T, router->num_experts, router->hidden, logits,
                                          stream));
 }
 
 moe_status moe_route(const moe_router* router, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
                      int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (router == nullptr || x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr || T < 0)
-    return MOE_ERR_INVALID_ARG;
+  if (router == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
   moe_status s = check_router(*router);
   if (s != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
   if (router->mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16)) return MOE_ERR_ALIGNMENT;
   if (ws == nullptr || ws_bytes < route_ws_bytes(*router, T)) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  if (T == 0) return MOE_OK;
   return run_route(*router, x_bf16, token_ids, T, topk_ids, topk_w, at<float>(ws, kHeader), at<int32_t>(ws, 0),
                    stream);
 }
 
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,
                        int32_t* perm, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (topk_ids == nullptr || expert_offsets == nullptr || perm == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
   if (E < 1 || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (k < 1 || k > E || k > 8) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (topk_ids == nullptr || expert_offsets == nullptr || perm == nullptr) return MOE_ERR_INVALID_ARG;
   if (ws == nullptr || ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  if (T == 0) return MOE_OK;
   return hip_status(launch_permute(topk_ids, T * k, E, expert_offsets, perm, at<int32_t>(ws, 0), stream));
 }
 
 moe_status moe_expert_ffn(const moe_experts* routed, const moe_experts* shared, const uint16_t* x_bf16, int32_t T,
                           int32_t k, const int32_t* expert_offsets, const int32_t* perm, float* y_slot,
                           float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (routed == nullptr || x_bf16 == nullptr || expert_offsets == nullptr || perm == nullptr || y_slot == nullptr ||
-      T < 0)
-    return MOE_ERR_INVALID_ARG;
+  if (routed == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
   const int E = routed->gate.num_experts;
   moe_status s = check_experts(*routed, E, 0);
   if (s != MOE_OK) return s;
   if (E < 1 || E > 1024) return MOE_ERR_UNSUPPORTED;
   if (k < 1 || k > E || k > 8) return MOE_ERR_INVALID_ARG;
+  if (shared && (s = check_experts(*shared, 1, routed->gate.cols)) != MOE_OK) return s;
+  if (T == 0) return MOE_OK;
+  if (x_bf16 == nullptr || expert_offsets == nullptr || perm == nullptr || y_slot == nullptr)
+    return MOE_ERR_INVALID_ARG;
   if (shared) {
-    if ((s = check_experts(*shared, 1, routed->gate.cols)) != MOE_OK) return s;
     if (y_shared == nullptr) return MOE_ERR_INVALID_ARG;
     if (!aligned(y_shared, 16)) return MOE_ERR_ALIGNMENT;
   }
   if (!aligned(x_bf16, 16) || !aligned(y_slot, 16)) return MOE_ERR_ALIGNMENT;
   if (ws == nullptr || ws_bytes < ffn_ws_bytes(*routed, shared, T, k)) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  if (T == 0) return MOE_OK;
   uint16_t* h = at<uint16_t>(ws, kHeader);
   uint16_t* h_sh = at<uint16_t>(ws, kHeader + align_up(static_cast<size_t>(T) * k * routed->gate.rows * 2));
   return run_ffn(*routed, shared, x_bf16, T, k, E, expert_offsets, perm, y_slot, y_shared, h, h_sh, stream);
@@ -294,27 +296,29 @@ moe_status moe_expert_ffn(const moe_experts* routed, const moe_experts* shared, 
 
 moe_status moe_combine(const float* y_slot, const float* topk_w, const float* y_shared, int32_t T, int32_t k,
                        int32_t d, int32_t out_dtype, void* out, hipStream_t stream) {
-  if (y_slot == nullptr || topk_w == nullptr || out == nullptr || T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || k < 1 || d < 1) return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARG;
   if (d % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (y_slot == nullptr || topk_w == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned(y_slot, 16) || !aligned(out, 8) || (y_shared && !aligned(y_shared, 16))) return MOE_ERR_ALIGNMENT;
   if (out_dtype == MOE_OUT_F32 && !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
-  if (T == 0) return MOE_OK;
   return hip_status(launch_combine(y_slot, topk_w, y_shared, T, k, d, out_dtype == MOE_OUT_F32, out, stream));
 }
 
 moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
                        int32_t out_dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (x_bf16 == nullptr || out == nullptr || T < 0) return MOE_ERR_INVALID_ARG;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
   moe_status s = check_layer(layer);
   if (s != MOE_OK) return s;
   const moe_layer& L = *layer;
-  if (L.router.mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (x_bf16 == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (L.router.mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
   if (ws == nullptr) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  if (T == 0) return MOE_OK;
   const FwdLayout f = forward_layout(L, T);
   if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
   const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;

@@ -66,8 +66,11 @@ def test_zero_tokens_launches_nothing():
     cfg = synth.config("tiny")
     dl = qm.DeviceLayer.from_host(synth.gen_layer(cfg))
     x = torch.empty((0, cfg.d), dtype=torch.int16, device="cuda")
-    out = qm.forward(dl, x, out_dtype="f32", ws=dl.workspace(1))
+    ws = dl.workspace(1)
+    out = qm.forward(dl, x, out_dtype="f32", ws=ws)
     assert out.shape == (0, cfg.d)
+    st = qm.forward_staged(dl, x, ws=ws)
+    assert st.out.shape == (0, cfg.d) and st.ids.shape == (0, cfg.top_k)
 
 
 def test_out_of_range_token_id_sets_error_word():
