@@ -80,6 +80,16 @@ def kernel_bytes(name, cfg, dl, T, touched):
         return sh.down.nbytes_per_expert() + T * cfg.I_shared * 2 + T * d * 4
     if name == "combine":
         return tk * d * 4 + tk * 4 + (T * d * 4 if sh is not None else 0) + T * d * 2
+    # fused small-batch path
+    sh_gu = sh.gate.nbytes_per_expert() + sh.up.nbytes_per_expert() + T * cfg.I_shared * 2 if sh is not None else 0
+    sh_dn = sh.down.nbytes_per_expert() + T * cfg.I_shared * 2 if sh is not None else 0
+    if name == "dec_router":
+        return E * d * 4 + T * d * 2 + T * E * 16 + sh_gu
+    if name == "dec_gateup":
+        return (touched * (r.gate.nbytes_per_expert() + r.up.nbytes_per_expert()) + T * E * 12 + T * d * 2
+                + tk * I * 2 + tk * 8)
+    if name == "dec_down_combine":
+        return touched * r.down.nbytes_per_expert() + sh_dn + T * E * 4 + tk * I * 2 + T * d * 2
     raise KeyError(name)
 
 

@@ -133,7 +133,7 @@ typedef struct {
  *    fp32 logits; no bias.
  *  weight : fp32 [E][hidden]; bias : fp32 [E] or NULL; tid2eid : int32
  *  [vocab][top_k] (hash mode only). 1 <= top_k <= min(E, 8), E <= 1024,
- *  hidden % 8 == 0.
+ *  hidden % 32 == 0.
  */
 typedef struct {
   int32_t mode;        /* moe_route_mode */
@@ -161,7 +161,8 @@ typedef struct {
  * invalid layer). The same size serves every other entry point. */
 size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens);
 
-/* Clear the workspace's device error word (a small kernel; capturable). */
+/* Zero the workspace header, which holds the device error word (a small
+ * kernel; capturable). */
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Step 1. x_bf16 [T][hidden]; token_ids int32 [T] (hash mode, else may be

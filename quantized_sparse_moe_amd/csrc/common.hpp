@@ -50,6 +50,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Exchange with a partner lane that differs in bit log2(mask): masks 1 and 2
+// are quad permutations, 4 and 8 the half-row / row mirrors (which flip the
+// target bit too), 16 and 32 go through ds_bpermute. For sums the pairing
+// only needs to flip the bit; the six pairings together reach all 64 lanes.
+__device__ __forceinline__ float xchg(float v, int mask) {
+  switch (mask) {
+    case 1: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    case 2: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+    case 4: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+    case 8: return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+    default: return __shfl_xor(v, mask);
+  }
+}
+
 // Reduce N values (N a power of two, N <= 64) across the wave at once.
 // Each halving step keeps half of the values per lane and exchanges the other
 // half with the partner lane, so the cost is about N + 6 shuffles instead of
@@ -69,12 +83,13 @@ __device__ __forceinline__ float wave_reduce_multi(const float (&v)[N]) {
     for (int i = 0; i < n / 2; ++i) {
       float send = upper ? cur[i] : cur[i + n / 2];
       float keep = upper ? cur[i + n / 2] : cur[i];
-      cur[i] = keep + __shfl_xor(send, mask);
+      cur[i] = keep + xchg(send, mask);
     }
     mask >>= 1;
   }
   float r = cur[0];
-  for (; mask >= 1; mask >>= 1) r += __shfl_xor(r, mask);
+#pragma unroll
+  for (; mask >= 1; mask >>= 1) r += xchg(r, mask);
   return r;
 }
 
@@ -120,5 +135,21 @@ __device__ __forceinline__ int find_bucket_expert(const int32_t* __restrict__ of
 __device__ __forceinline__ void set_device_error(int32_t* err, int code) {
   if (err) atomicOr(err, code);
 }
+
+// Optional phase timeline for performance analysis builds (-DQSMOE_TIMELINE):
+// thread 0 of a workgroup records the 100 MHz wall clock at a phase boundary.
+#ifdef QSMOE_TIMELINE
+constexpr int kTimelineRegion = 1 << 15;  // entries per kernel region
+extern __device__ uint64_t g_timeline[4 * kTimelineRegion];
+#define QSMOE_TL(region, slot)                                                                   \
+  do {                                                                                          \
+    if (threadIdx.x == 0 && blockIdx.x * 8 + (slot) < kTimelineRegion)                          \
+      g_timeline[(region) * kTimelineRegion + blockIdx.x * 8 + (slot)] = wall_clock64();        \
+  } while (0)
+#else
+#define QSMOE_TL(region, slot) \
+  do {                         \
+  } while (0)
+#endif
 
 }  // namespace qsmoe

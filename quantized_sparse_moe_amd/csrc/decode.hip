@@ -1,0 +1,386 @@
+// Fused small-batch (decode) path of the layer: three launches instead of
+// eight when a step has at most 4 tokens, top-k routing and at most 256
+// experts.
+//
+//   1. k_dec_router: the fp32 router logits (one wave per expert) with each
+//      expert's score and ranking key, and on the remaining workgroups the
+//      shared expert's gate/up + SwiGLU (no routing needed).
+//   2. k_dec_gateup: each workgroup selects the top-k from the keys (same
+//      selection as moe_route, so the ids are bit-identical) and streams the
+//      selected experts' gate/up rows; no bucketing kernel is needed because
+//      each (token, slot) is its own bucket when tokens are this few.
+//   3. k_dec_down_combine: per output row, the k selected experts' down rows
+//      and the shared expert's down row are dotted with their own h vectors
+//      (all held in registers), weighted by the router weights and summed in
+//      one reduction: down projection, shared expert and combine in one pass,
+//      without atomics (one writer per output element).
+//
+// The layer's definition is that of the general path (router: fp32 gate of
+// mlx-lm PR "Add DeepSeek-v4 (Flash/Pro)", sqrtsoftplus of
+// "mlx-community / DeepSeek-V4-Flash-4bit"; experts: the same PR's stacked
+// gate/up/down; shared expert of "DeepSeek-V4-Flash-MLX-4bit"); only the
+// order of the fp32 additions in the combine differs.
+#include <algorithm>
+
+#include "ffn_core.hpp"
+#include "router_core.hpp"
+
+namespace qsmoe {
+
+#ifdef QSMOE_TIMELINE
+__device__ uint64_t g_timeline[4 * kTimelineRegion];
+
+hipError_t timeline_copy(void* host, size_t bytes) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
+
+constexpr int kDecMaxT = 4;
+constexpr int kDecMaxK = 8;
+
+
+// Launch 1: router logits of four experts per workgroup (one per wave), with
+// each expert's score and ranking key for every token; the remaining
+// workgroups stream the shared expert's gate/up, which needs no routing.
+template <int TT, int SCPL, int SNT>
+__global__ __launch_bounds__(256) void k_dec_router(DecodeArgs a) {
+  QSMOE_TL(0, 0);
+  if (static_cast<int>(blockIdx.x) < a.n_logit_blocks) {
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e < a.E) logits_wave<TT>(a.x, a.wr, a.T, a.E, a.d, e, 0, a.logits, a.bias, a.keys, a.scores);
+  } else if constexpr (SNT > 0) {
+    StreamArgs sa{a.sgate, a.sup, a.x, a.T, a.k, 1, nullptr, nullptr, 1, a.h_sh, nullptr};
+    ffn_stream_body<0, 8, SCPL, SNT, true>(sa, blockIdx.x - a.n_logit_blocks, gridDim.x - a.n_logit_blocks, nullptr,
+                                           nullptr);
+  }
+  __syncthreads();
+  QSMOE_TL(0, 7);
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2. Every workgroup first selects each token's top-k from the
+// launch-1 keys (wave t: token t, keys in registers; same selection as
+// moe_route, so the ids are bit-identical; workgroup 0 also publishes ids and
+// weights for launch 3), then streams the (token, slot) x row units of the
+// selected experts' gate/up, split evenly over all waves.
+template <int F, int B, int CPL>
+__global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
+  __shared__ int32_t s_ids[kDecMaxT * kDecMaxK];
+  QSMOE_TL(1, 0);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  if (wave < a.T) {
+    uint64_t key[4];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = e < a.E;
+      const size_t o = static_cast<size_t>(wave) * a.E + (ok ? e : 0);
+      key[i] = a.keys[o];
+      sc[i] = a.scores[o];
+      key[i] = ok ? key[i] : 0;
+    }
+    int id;
+    float wt;
+    topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
+    if (lane < a.k) {
+      s_ids[wave * a.k + lane] = id;
+      if (blockIdx.x == 0) {
+        a.ids[wave * a.k + lane] = id;
+        a.w[wave * a.k + lane] = wt;
+      }
+    }
+  }
+  __syncthreads();
+  QSMOE_TL(1, 1);
+  const int rows = a.gate.rows, nchunks = a.gate.cols >> 5;
+  const int64_t total = static_cast<int64_t>(a.T) * a.k * rows;
+  const int64_t W = static_cast<int64_t>(gridDim.x) * 4, gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  int64_t u = total * gw / W;
+  const int64_t u_end = total * (gw + 1) / W;
+  while (u < u_end) {
+    const int slot = static_cast<int>(u / rows);
+    const int r_begin = static_cast<int>(u - static_cast<int64_t>(slot) * rows);
+    const int r_end = static_cast<int>(min<int64_t>(rows, r_begin + (u_end - u)));
+    const int t = slot / a.k;
+    const uint16_t* xrow[1] = {a.x + static_cast<size_t>(t) * a.d};
+    const bool xvalid[1] = {true};
+    XRaw<CPL, 1> xw;
+    load_x_raw<CPL, 1>(xw, xrow, lane, nchunks);
+    const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
+    const QMat q0 = expert_slice(a.gate, e), q1 = expert_slice(a.up, e);
+    uint16_t* hs = a.h + static_cast<size_t>(slot) * rows;
+    stream_rows<F, B, CPL, 1, true>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
+                                    [&](int, int r, float g, float up) {
+                                      hs[r] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * up));
+                                    });
+    u += r_end - r_begin;
+  }
+  __syncthreads();
+  QSMOE_TL(1, 7);
+}
+
+// ---------------------------------------------------------------------------
+// Partial (this lane's) dot of one row with token j's activations.
+template <int F, int B, int CPL, int NT>
+__device__ __forceinline__ float row_dot_one(const RowRegs<F, B, CPL>& r, const XRegs<F, B, CPL, NT>& xr, int j,
+                                             int lane, int nchunks) {
+  using C = Codec<F, B>;
+  float acc = 0.0f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const bool ok = lane + 64 * m < nchunks;
+    uint32_t p[16];
+    C::pairs(r.w[m], p);
+    float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      d0 = dot2_bf16(p[i], xr.px[j][m][i], d0);
+      d1 = dot2_bf16(p[i + 1], xr.px[j][m][i + 1], d1);
+    }
+    const float d = d0 + d1;
+    if constexpr (F == 0) {
+      const float s = ok ? f16_to_f32(static_cast<uint16_t>(r.s[m])) : 0.0f;
+      const float b = ok ? f16_to_f32(static_cast<uint16_t>(r.b[m])) : 0.0f;
+      acc += s * d + (b - C::kOff * s) * xr.xs[j][m];
+    } else {
+      acc += d * (ok ? e8m0_to_f32(r.s[m]) : 0.0f);
+    }
+  }
+  return acc;
+}
+
+constexpr int kDecRows = 2;  // output rows per batch per wave
+
+template <int F, int B, int K, bool SH>
+struct DownBatch {
+  RowRegs<F, B, 1> r[kDecRows][K];
+  RowRegs<0, 8, 1> rs[kDecRows];
+};
+
+template <int F, int B, int K, bool SH>
+__device__ __forceinline__ void dec_load_down(DownBatch<F, B, K, SH>& b, const QMat (&qd)[K], const QMat& qs, int r0,
+                                              int r_end, int lane, int nchunks, int nchunks_sh) {
+#pragma unroll
+  for (int i = 0; i < kDecRows; ++i) {
+    const int r = min(r0 + i, r_end - 1);
+#pragma unroll
+    for (int j = 0; j < K; ++j) load_row<F, B, 1>(b.r[i][j], qd[j], r, lane, nchunks);
+    if constexpr (SH) load_row<0, 8, 1>(b.rs[i], qs, r, lane, nchunks_sh);
+  }
+}
+
+template <int F, int B, int K, bool SH>
+__device__ __forceinline__ void dec_compute_down(const DownBatch<F, B, K, SH>& b, const XRegs<F, B, 1, K>& hx,
+                                                 const XRegs<0, 8, 1, 1>& hsx, const float (&wj)[K],
+                                                 const DecodeArgs& a, int t, int r0, int r_end, int lane,
+                                                 int nchunks, int nchunks_sh) {
+  float acc[kDecRows];
+#pragma unroll
+  for (int i = 0; i < kDecRows; ++i) {
+    float v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < K; ++j) v += wj[j] * row_dot_one<F, B, 1, K>(b.r[i][j], hx, j, lane, nchunks);
+    if constexpr (SH) v += row_dot_one<0, 8, 1, 1>(b.rs[i], hsx, 0, lane, nchunks_sh);
+    acc[i] = v;
+  }
+  const float y = wave_reduce_multi<kDecRows>(acc);
+  const int ri = reduce_multi_index<kDecRows>(lane);
+  if (reduce_multi_writer<kDecRows>(lane) && r0 + ri < r_end) {
+    const size_t o = static_cast<size_t>(t) * a.down.rows + r0 + ri;
+    if (a.out_f32)
+      static_cast<float*>(a.out)[o] = y;
+    else
+      static_cast<uint16_t*>(a.out)[o] = static_cast<uint16_t>(f32_to_bf16_rne(y));
+  }
+}
+
+// Launch 3: per (token, output row) unit, the k selected experts' down rows
+// and the shared expert's down row against their own h vectors, weighted and
+// summed in one reduction; double-buffered like the streaming core.
+template <int F, int B, int K, bool SH>
+__global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
+  QSMOE_TL(2, 0);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int rows = a.down.rows, I = a.down.cols, nchunks = I >> 5;
+  const int Ish = SH ? a.sdown.cols : 32, nchunks_sh = Ish >> 5;
+  const int64_t total = static_cast<int64_t>(a.T) * rows;
+  const int64_t W = static_cast<int64_t>(gridDim.x) * 4, gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  int64_t u = total * gw / W;
+  const int64_t u_end = total * (gw + 1) / W;
+  while (u < u_end) {
+    const int t = static_cast<int>(u / rows);
+    const int r_begin = static_cast<int>(u - static_cast<int64_t>(t) * rows);
+    const int r_end = static_cast<int>(min<int64_t>(rows, r_begin + (u_end - u)));
+    // ids and weights first, then the h rows, then wait for the ids only
+    int id_raw[K];
+    float wj[K];
+    const uint16_t* hrow[K];
+    bool hvalid[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      const bool ok = j < a.k;
+      const int jj = ok ? j : 0;
+      id_raw[j] = a.ids[t * a.k + jj];
+      wj[j] = a.w[t * a.k + jj];
+      wj[j] = ok ? wj[j] : 0.0f;
+      hrow[j] = a.h + static_cast<size_t>(t * a.k + jj) * I;
+      hvalid[j] = ok;
+    }
+    XRaw<1, K> hw;
+    load_x_raw<1, K>(hw, hrow, lane, nchunks);
+    XRaw<1, 1> hsw;
+    const uint16_t* srow[1] = {a.h_sh + static_cast<size_t>(t) * Ish};
+    const bool sv[1] = {true};
+    if constexpr (SH) load_x_raw<1, 1>(hsw, srow, lane, nchunks_sh);
+    QMat qd[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      qd[j] = expert_slice(a.down, min(max(__builtin_amdgcn_readfirstlane(id_raw[j]), 0), a.E - 1));
+    DownBatch<F, B, K, SH> A, Bb;
+    int r = r_begin;
+    dec_load_down<F, B, K, SH>(A, qd, a.sdown, r, r_end, lane, nchunks, nchunks_sh);
+    XRegs<F, B, 1, K> hx;
+    finish_x<F, B, 1, K>(hx, hw, hvalid, lane, nchunks);
+    XRegs<0, 8, 1, 1> hsx;
+    if constexpr (SH) finish_x<0, 8, 1, 1>(hsx, hsw, sv, lane, nchunks_sh);
+    QSMOE_TL(2, 1);
+    while (true) {
+      dec_load_down<F, B, K, SH>(Bb, qd, a.sdown, r + kDecRows, r_end, lane, nchunks, nchunks_sh);
+      dec_compute_down<F, B, K, SH>(A, hx, hsx, wj, a, t, r, r_end, lane, nchunks, nchunks_sh);
+      if (r + kDecRows >= r_end) break;
+      dec_load_down<F, B, K, SH>(A, qd, a.sdown, r + 2 * kDecRows, r_end, lane, nchunks, nchunks_sh);
+      dec_compute_down<F, B, K, SH>(Bb, hx, hsx, wj, a, t, r + kDecRows, r_end, lane, nchunks, nchunks_sh);
+      if (r + 2 * kDecRows >= r_end) break;
+      r += 2 * kDecRows;
+    }
+    u += r_end - r_begin;
+  }
+  __syncthreads();
+  QSMOE_TL(2, 7);
+}
+
+// ---------------------------------------------------------------------------
+static int dec_cpl(int cols) { return cols <= 2048 ? 1 : (cols <= 4096 ? 2 : 4); }
+
+bool decode_path_supported(const DecodeArgs& a) {
+  if (a.T < 1 || a.T > kDecMaxT || a.k > kDecMaxK || a.E > 256 || a.d % 32 != 0) return false;
+  if (a.down.cols > 2048) return false;
+  if (a.has_shared) {
+    if (a.sgate.fmt != 0 || a.sgate.bits != 8 || a.sdown.fmt != 0 || a.sdown.bits != 8) return false;
+    if (a.sdown.cols > 2048) return false;
+  }
+  return true;
+}
+
+// Grid sizing of launches 2 and 3: at most kDecMaxWg workgroups, at least
+// the given rows per wave.
+#ifndef QSMOE_DEC_MAX_WG
+#define QSMOE_DEC_MAX_WG 512
+#endif
+#ifndef QSMOE_DEC_GU_MIN_ROWS
+#define QSMOE_DEC_GU_MIN_ROWS 2
+#endif
+#ifndef QSMOE_DEC_DN_MIN_ROWS
+#define QSMOE_DEC_DN_MIN_ROWS 4
+#endif
+
+// Workgroups for `units` rows with at least `min_rows` rows per wave.
+static unsigned dec_grid(int64_t units, int min_rows = 2) {
+  const int64_t per_wg = 4 * min_rows;
+  return static_cast<unsigned>(
+      std::max<int64_t>(1, std::min<int64_t>((units + per_wg - 1) / per_wg, QSMOE_DEC_MAX_WG)));
+}
+
+#define QSMOE_DEC_FMT(FMT_, BITS_, ...)                      \
+  if ((FMT_) == 0 && (BITS_) == 4) {                         \
+    constexpr int F = 0, B = 4;                              \
+    __VA_ARGS__                                              \
+  } else if ((FMT_) == 0 && (BITS_) == 2) {                  \
+    constexpr int F = 0, B = 2;                              \
+    __VA_ARGS__                                              \
+  } else if ((FMT_) == 0 && (BITS_) == 3) {                  \
+    constexpr int F = 0, B = 3;                              \
+    __VA_ARGS__                                              \
+  } else if ((FMT_) == 0 && (BITS_) == 8) {                  \
+    constexpr int F = 0, B = 8;                              \
+    __VA_ARGS__                                              \
+  } else {                                                   \
+    constexpr int F = 1, B = 4;                              \
+    __VA_ARGS__                                              \
+  }
+
+// Tokens per pass of the shared expert's gate/up (0: no shared expert).
+static int dec_shared_nt(const DecodeArgs& a, int cpl) {
+  if (!a.has_shared) return 0;
+  int nt = a.T <= 1 ? 1 : (a.T <= 2 ? 2 : 4);
+  while (nt * cpl > 4) nt >>= 1;
+  return nt;
+}
+
+hipError_t launch_dec_router(const DecodeArgs& a0, hipStream_t s) {
+  DecodeArgs a = a0;
+  a.n_logit_blocks = (a.E + 3) / 4;
+  const int scpl = a.has_shared ? dec_cpl(a.sgate.cols) : 1;
+  const int snt = dec_shared_nt(a, scpl);
+  unsigned grid = a.n_logit_blocks;
+  if (snt > 0) grid += dec_grid(static_cast<int64_t>((a.T + snt - 1) / snt) * a.sgate.rows, 2);
+  const int tt = a.T <= 1 ? 1 : (a.T <= 2 ? 2 : 4);
+#define QSMOE_K1(CP, NT_)                                                                   \
+  do {                                                                                      \
+    if (tt == 1)                                                                            \
+      hipLaunchKernelGGL((k_dec_router<1, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
+    else if (tt == 2)                                                                       \
+      hipLaunchKernelGGL((k_dec_router<2, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
+    else                                                                                    \
+      hipLaunchKernelGGL((k_dec_router<4, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
+  } while (0)
+  if (snt == 0) QSMOE_K1(1, 0);
+  else if (scpl == 1 && snt == 1) QSMOE_K1(1, 1);
+  else if (scpl == 1 && snt == 2) QSMOE_K1(1, 2);
+  else if (scpl == 1) QSMOE_K1(1, 4);
+  else if (scpl == 2 && snt == 1) QSMOE_K1(2, 1);
+  else if (scpl == 2) QSMOE_K1(2, 2);
+  else QSMOE_K1(4, 1);
+#undef QSMOE_K1
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
+  const int cpl = dec_cpl(a.gate.cols);
+  const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.k * a.gate.rows, QSMOE_DEC_GU_MIN_ROWS)), block(256);
+  QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
+    if (cpl == 1)
+      hipLaunchKernelGGL((k_dec_gateup<F, B, 1>), grid, block, 0, s, a);
+    else if (cpl == 2)
+      hipLaunchKernelGGL((k_dec_gateup<F, B, 2>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((k_dec_gateup<F, B, 4>), grid, block, 0, s, a);
+  })
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.down.rows, QSMOE_DEC_DN_MIN_ROWS)), block(256);
+  const size_t lds = 0;
+  const int K = a.k <= 2 ? 2 : (a.k <= 4 ? 4 : (a.k <= 6 ? 6 : 8));
+#define QSMOE_K3(K_)                                                                                   \
+  do {                                                                                                 \
+    if (a.has_shared)                                                                                  \
+      hipLaunchKernelGGL((k_dec_down_combine<F, B, K_, true>), grid, block, lds, s, a);                \
+    else                                                                                               \
+      hipLaunchKernelGGL((k_dec_down_combine<F, B, K_, false>), grid, block, lds, s, a);               \
+  } while (0)
+  QSMOE_DEC_FMT(a.down.fmt, a.down.bits, {
+    if (K == 2) QSMOE_K3(2);
+    else if (K == 4) QSMOE_K3(4);
+    else if (K == 6) QSMOE_K3(6);
+    else QSMOE_K3(8);
+  })
+#undef QSMOE_K3
+  return hipGetLastError();
+}
+
+}  // namespace qsmoe

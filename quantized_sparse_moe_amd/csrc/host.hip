@@ -13,7 +13,9 @@ using namespace qsmoe;
 
 namespace {
 
-constexpr size_t kHeader = 256;  // error word + padding at the start of every workspace
+// Every workspace starts with a 256-byte header; int32 [0] is the sticky
+// device error word. moe_workspace_init zeroes the header.
+constexpr size_t kHeader = 256;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -79,7 +81,7 @@ moe_status check_router(const moe_router& r) {
   if (r.weight == nullptr) return MOE_ERR_INVALID_ARG;
   if (r.num_experts < 1 || r.num_experts > 1024) return MOE_ERR_UNSUPPORTED;
   if (r.top_k < 1 || r.top_k > r.num_experts || r.top_k > 8) return MOE_ERR_INVALID_ARG;
-  if (r.hidden < 8 || r.hidden % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (r.hidden < 32 || r.hidden % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!aligned(r.weight, 16)) return MOE_ERR_ALIGNMENT;
   if (r.bias != nullptr && !aligned(r.bias, 4)) return MOE_ERR_ALIGNMENT;
   if (r.mode == MOE_ROUTE_HASH) {
@@ -111,7 +113,7 @@ size_t ffn_ws_bytes(const moe_experts& routed, const moe_experts* shared, int T,
 }
 
 struct FwdLayout {
-  size_t ids, w, logits, offsets, perm, h, h_sh, y_slot, y_sh, total;
+  size_t ids, w, logits, keys, offsets, perm, h, h_sh, y_slot, y_sh, total;
 };
 
 FwdLayout forward_layout(const moe_layer& L, int T) {
@@ -125,6 +127,8 @@ FwdLayout forward_layout(const moe_layer& L, int T) {
   o += align_up(tk * 4);
   f.logits = o;
   o += L.router.mode == MOE_ROUTE_TOPK ? align_up(static_cast<size_t>(T) * E * 4) : 0;
+  f.keys = o;  // small-batch path only (T <= 4): ranking keys and scores
+  o += L.router.mode == MOE_ROUTE_TOPK && T <= 4 ? align_up(static_cast<size_t>(T) * E * 12) : 0;
   f.offsets = o;
   o += align_up((E + 1) * 4);
   f.perm = o;
@@ -227,7 +231,7 @@ size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens) {
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
   if (ws == nullptr || ws_bytes < kHeader) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  return hip_status(launch_fill_i32(static_cast<int32_t*>(ws), 0, 1, stream));
+  return hip_status(launch_fill_i32(static_cast<int32_t*>(ws), 0, static_cast<int>(kHeader / 4), stream));
 }
 
 moe_status moe_router_logits(const moe_router* router, const uint16_t* x_bf16, int32_t T, float* logits,
@@ -322,6 +326,40 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
   const FwdLayout f = forward_layout(L, T);
   if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
   const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;
+  if (L.router.mode == MOE_ROUTE_TOPK) {
+    DecodeArgs da{};
+    da.x = x_bf16;
+    da.T = T;
+    da.d = d;
+    da.E = E;
+    da.k = k;
+    da.routed_scale = L.router.routed_scale;
+    da.wr = L.router.weight;
+    da.bias = L.router.bias;
+    da.logits = at<float>(ws, f.logits);
+    da.keys = at<uint64_t>(ws, f.keys);
+    da.scores = reinterpret_cast<float*>(at<uint64_t>(ws, f.keys) + static_cast<size_t>(T) * E);
+    da.gate = to_qmat(L.routed.gate);
+    da.up = to_qmat(L.routed.up);
+    da.down = to_qmat(L.routed.down);
+    da.h = at<uint16_t>(ws, f.h);
+    da.has_shared = L.shared != nullptr;
+    if (L.shared) {
+      da.sgate = to_qmat(L.shared->gate);
+      da.sup = to_qmat(L.shared->up);
+      da.sdown = to_qmat(L.shared->down);
+      da.h_sh = at<uint16_t>(ws, f.h_sh);
+    }
+    da.out = out;
+    da.out_f32 = out_dtype == MOE_OUT_F32;
+    da.ids = at<int32_t>(ws, f.ids);
+    da.w = at<float>(ws, f.w);
+    if (decode_path_supported(da)) {
+      if (mark(launch_dec_router(da, stream), "dec_router", stream) != hipSuccess) return MOE_ERR_HIP;
+      if (mark(launch_dec_gateup(da, stream), "dec_gateup", stream) != hipSuccess) return MOE_ERR_HIP;
+      return hip_status(mark(launch_dec_down_combine(da, stream), "dec_down_combine", stream));
+    }
+  }
   int32_t* err = at<int32_t>(ws, 0);
   int32_t* ids = at<int32_t>(ws, f.ids);
   float* w = at<float>(ws, f.w);
@@ -354,6 +392,11 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
   if (s == MOE_OK && p.overflow) return MOE_ERR_INVALID_ARG;
   return s;
 }
+
+#ifdef QSMOE_TIMELINE
+// Analysis builds only: copy the phase timeline to host memory.
+moe_status moe_debug_timeline(void* host, size_t bytes) { return hip_status(timeline_copy(host, bytes)); }
+#endif
 
 moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream) {
   if (ws == nullptr || code_out == nullptr) return MOE_ERR_INVALID_ARG;

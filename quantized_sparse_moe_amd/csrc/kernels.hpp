@@ -60,12 +60,42 @@ struct DownArgs {
 };
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
+// Fused small-batch path (T <= 4 tokens, top-k routing) ------------------------
+struct DecodeArgs {
+  const uint16_t* x;       // bf16 [T][d]
+  int32_t T, d, E, k;
+  float routed_scale;
+  const float* wr;         // router weight fp32 [E][d]
+  const float* bias;       // fp32 [E] or null
+  float* logits;           // workspace fp32 [T][E]
+  uint64_t* keys;          // workspace [T][E] ranking keys (score + bias, ~index)
+  float* scores;           // workspace fp32 [T][E] sqrtsoftplus scores
+  QMat gate, up, down;     // routed experts
+  uint16_t* h;             // workspace bf16 [T*k][I] (slot order)
+  int32_t has_shared;
+  QMat sgate, sup, sdown;  // shared expert (affine 8-bit) when has_shared
+  uint16_t* h_sh;          // workspace bf16 [T][I_shared]
+  void* out;               // bf16 or fp32 [T][d]
+  int32_t out_f32;
+  int32_t n_logit_blocks;  // workgroups of launch 1 that compute logits (set by its launcher)
+  int32_t* ids;            // workspace int32 [T][k], written by launch 2
+  float* w;                // workspace fp32 [T][k], written by launch 2
+};
+bool decode_path_supported(const DecodeArgs& a);
+hipError_t launch_dec_router(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s);
+
 // Combine --------------------------------------------------------------------
 hipError_t launch_combine(const float* y_slot, const float* w, const float* y_shared, int T, int k, int d,
                           int out_f32, void* out, hipStream_t s);
 
 // Workspace ------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
+
+#ifdef QSMOE_TIMELINE
+hipError_t timeline_copy(void* host, size_t bytes);
+#endif
 
 // Does a GEMV kernel exist for this projection shape/format?
 bool gemv_supported(const QMat& m);

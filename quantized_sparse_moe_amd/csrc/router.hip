@@ -6,48 +6,19 @@
 // scores are sqrt(softplus(l)) ("mlx-community / DeepSeek-V4-Flash-4bit",
 // "Architecture") evaluated in the overflow-free logaddexp form the same PR's
 // review notes ask for.
-#include "common.hpp"
 #include "kernels.hpp"
+#include "router_core.hpp"
 
 namespace qsmoe {
 
 // ---------------------------------------------------------------------------
-// Logits, few tokens: one wave per (expert, TT tokens); lanes stride the
-// hidden dimension 8 values at a time (32 B of Wr, 16 B of x per token).
+// Logits, few tokens: one wave per (expert, TT tokens).
 // ---------------------------------------------------------------------------
 template <int TT>
 __global__ __launch_bounds__(256) void k_logits_gemv(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                      int T, int E, int d, float* __restrict__ logits) {
-  const int lane = lane_id();
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t0 = blockIdx.y * TT;
-  if (e >= E) return;
-  float acc[TT];
-#pragma unroll
-  for (int j = 0; j < TT; ++j) acc[j] = 0.0f;
-  const float* wrow = wr + static_cast<size_t>(e) * d;
-  for (int base = lane * 8; base < d; base += 64 * 8) {
-    const float4 w0 = *reinterpret_cast<const float4*>(wrow + base);
-    const float4 w1 = *reinterpret_cast<const float4*>(wrow + base + 4);
-#pragma unroll
-    for (int j = 0; j < TT; ++j) {
-      const int t = min(t0 + j, T - 1);
-      const uint4 xv = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(t) * d + base);
-      float a = acc[j];
-      a = fmaf(bf16_to_f32(xv.x & 0xffffu), w0.x, a);
-      a = fmaf(bf16_to_f32(xv.x >> 16), w0.y, a);
-      a = fmaf(bf16_to_f32(xv.y & 0xffffu), w0.z, a);
-      a = fmaf(bf16_to_f32(xv.y >> 16), w0.w, a);
-      a = fmaf(bf16_to_f32(xv.z & 0xffffu), w1.x, a);
-      a = fmaf(bf16_to_f32(xv.z >> 16), w1.y, a);
-      a = fmaf(bf16_to_f32(xv.w & 0xffffu), w1.z, a);
-      a = fmaf(bf16_to_f32(xv.w >> 16), w1.w, a);
-      acc[j] = a;
-    }
-  }
-  const float r = wave_reduce_multi<TT>(acc);
-  const int j = reduce_multi_index<TT>(lane);
-  if (reduce_multi_writer<TT>(lane) && t0 + j < T) logits[static_cast<size_t>(t0 + j) * E + e] = r;
+  if (e < E) logits_wave<TT>(x, wr, T, E, d, e, blockIdx.y * TT, logits);
 }
 
 // ---------------------------------------------------------------------------
@@ -110,77 +81,24 @@ __global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t* __restrict
   }
 }
 
-// Order-preserving map of an fp32 key and expert index to a 64-bit value:
-// larger key first, equal keys -> lower index first.
-__device__ __forceinline__ uint64_t pack_key(float key, int e) {
-  const uint32_t u = __float_as_uint(key);
-  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(0xffffffffu - static_cast<uint32_t>(e));
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token. Each lane holds EPL experts (e = lane + 64 i).
-// k rounds of a wave arg-max over packed (key, ~index); the winner's owner
-// retires it. Weights are the selected unbiased scores renormalised.
+// Top-k: one wave per token (keys staged in LDS, 12 bytes per expert).
 // ---------------------------------------------------------------------------
-template <int EPL>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
                                               int T, int E, int k, float routed_scale, int32_t* __restrict__ ids,
                                               float* __restrict__ w) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  extern __shared__ uint64_t lds_keys[];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  float s[EPL];
-  uint64_t key[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + 64 * i;
-    if (e < E) {
-      s[i] = sqrtsoftplus(logits[static_cast<size_t>(t) * E + e]);
-      key[i] = pack_key(s[i] + (bias ? bias[e] : 0.0f), e);
-    } else {
-      s[i] = 0.0f;
-      key[i] = 0;
-    }
-  }
-  int sel_e = 0;
-  float sel_s = 0.0f, total = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
-    float se = 0.0f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (key[i] == best) {
-        se = s[i];
-        key[i] = 0;
-      }
-    }
-    const float sj = __shfl(se, e & 63);
-    total += sj;
-    if (lane == j) {
-      sel_e = e;
-      sel_s = sj;
-    }
-  }
+  uint64_t* s_key = lds_keys + static_cast<size_t>(wave) * E;
+  float* s_s = reinterpret_cast<float*>(lds_keys + static_cast<size_t>(4) * E) + static_cast<size_t>(wave) * E;
+  int id;
+  float wt;
+  topk_wave(logits + static_cast<size_t>(t) * E, bias, E, k, routed_scale, s_key, s_s, id, wt);
   if (lane < k) {
-    const float wj = total > 0.0f ? sel_s / total : 1.0f / static_cast<float>(k);
-    ids[static_cast<size_t>(t) * k + lane] = sel_e;
-    w[static_cast<size_t>(t) * k + lane] = wj * routed_scale;
+    ids[static_cast<size_t>(t) * k + lane] = id;
+    w[static_cast<size_t>(t) * k + lane] = wt;
   }
 }
 
@@ -273,11 +191,11 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
 // ---------------------------------------------------------------------------
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E, int d, float* logits,
                                 hipStream_t s) {
-  if (T > 16 && d % 32 == 0) {
+  if (T > 16) {
     dim3 grid((E + 63) / 64, (T + 63) / 64);
     hipLaunchKernelGGL(k_logits_tiled, grid, dim3(256), 0, s, x, wr, T, E, d, logits);
   } else if (T == 1) {
-    hipLaunchKernelGGL(k_logits_gemv<1>, dim3((E + 3) / 4, T), dim3(256), 0, s, x, wr, T, E, d, logits);
+    hipLaunchKernelGGL(k_logits_gemv<1>, dim3((E + 3) / 4, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else if (T == 2) {
     hipLaunchKernelGGL(k_logits_gemv<2>, dim3((E + 3) / 4, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else {
@@ -288,17 +206,8 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E
 
 hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k, float routed_scale,
                               int32_t* ids, float* w, hipStream_t s) {
-  dim3 grid((T + 3) / 4), block(256);
-  if (E <= 64)
-    hipLaunchKernelGGL(k_topk<1>, grid, block, 0, s, logits, bias, T, E, k, routed_scale, ids, w);
-  else if (E <= 128)
-    hipLaunchKernelGGL(k_topk<2>, grid, block, 0, s, logits, bias, T, E, k, routed_scale, ids, w);
-  else if (E <= 256)
-    hipLaunchKernelGGL(k_topk<4>, grid, block, 0, s, logits, bias, T, E, k, routed_scale, ids, w);
-  else if (E <= 512)
-    hipLaunchKernelGGL(k_topk<8>, grid, block, 0, s, logits, bias, T, E, k, routed_scale, ids, w);
-  else
-    hipLaunchKernelGGL(k_topk<16>, grid, block, 0, s, logits, bias, T, E, k, routed_scale, ids, w);
+  const size_t lds = static_cast<size_t>(4) * E * (sizeof(uint64_t) + sizeof(float));
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), lds, s, logits, bias, T, E, k, routed_scale, ids, w);
   return hipGetLastError();
 }
 
