@@ -28,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill)"
 
 
@@ -70,9 +71,9 @@ def kernel_bytes(name, cfg, dl, T, touched):
         return min(E, tk) * d * 4 + T * d * 2 + T * 4 + tk * 4 + tk * 8
     if name == "permute":
         return tk * 4 + (E + 1) * 4 + tk * 4
-    if name == "routed_gateup":
+    if name in ("routed_gateup", "routed_gateup_mfma"):
         return touched * (r.gate.nbytes_per_expert() + r.up.nbytes_per_expert()) + T * d * 2 + tk * I * 2
-    if name == "routed_down":
+    if name in ("routed_down", "routed_down_mfma"):
         return touched * r.down.nbytes_per_expert() + tk * I * 2 + tk * d * 4
     if name == "shared_gateup":
         return sh.gate.nbytes_per_expert() + sh.up.nbytes_per_expert() + T * d * 2 + T * cfg.I_shared * 2
@@ -91,6 +92,17 @@ def kernel_bytes(name, cfg, dl, T, touched):
     if name == "dec_down_combine":
         return touched * r.down.nbytes_per_expert() + sh_dn + T * E * 4 + tk * I * 2 + T * d * 2
     raise KeyError(name)
+
+
+def kernel_flops(name, cfg, T):
+    """Algorithmic flops of one launch of an MFMA expert kernel (2 per
+    multiply-add over every routed (token, expert) pair)."""
+    tk = T * cfg.top_k
+    if name == "routed_gateup_mfma":
+        return 2.0 * tk * cfg.d * 2 * cfg.I
+    if name == "routed_down_mfma":
+        return 2.0 * tk * cfg.I * cfg.d
+    return None
 
 
 def step_bytes(cfg, dl, T, touched):
@@ -225,7 +237,18 @@ def main():
     kern = {n: float(np.mean(v)) for n, v in sums.items()}
     dom = max(kern, key=kern.get)
     dom_bytes = kernel_bytes(dom, cfg, base, T, touched_mean)
-    achieved = dom_bytes / (kern[dom] * 1e-6) / 1e9
+    dom_flops = kernel_flops(dom, cfg, T)
+    if dom_flops is None:
+        achieved = dom_bytes / (kern[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_us": kern[dom]}
+    else:
+        achieved = dom_flops / (kern[dom] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "algorithmic_flops_per_launch": dom_flops, "algorithmic_bytes_per_launch": dom_bytes,
+                "avg_launch_us": kern[dom]}
 
     sbytes = step_bytes(cfg, base, T, touched_mean)
     rec = {
@@ -245,9 +268,7 @@ def main():
                    "timing": mode, "touched_experts_per_step": touched_mean},
         "hbm_gbps": sbytes / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": sbytes,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": kern[dom]},
+        "roofline": roof,
         "kernels_us": kern,
         "wall_s": wall,
         "setup_s": gen_s,

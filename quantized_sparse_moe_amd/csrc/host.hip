@@ -195,13 +195,21 @@ moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const u
     GateUpArgs g{to_qmat(shared->gate), to_qmat(shared->up), x, T, k, 1, nullptr, nullptr, 1, h_sh};
     if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) return MOE_ERR_HIP;
   }
+  // Grouped GEMM on the matrix cores once buckets average 16+ tokens.
+  const bool mfma = mfma_supported(to_qmat(routed.gate), to_qmat(routed.down)) &&
+                    static_cast<int64_t>(T) * k >= 16LL * E;
   GateUpArgs g{to_qmat(routed.gate), to_qmat(routed.up), x, T, k, E, offsets, perm, 0, h};
-  if (mark(launch_gateup(g, s), "routed_gateup", s) != hipSuccess) return MOE_ERR_HIP;
+  if (mfma) {
+    if (mark(launch_mfma_gateup(g, s), "routed_gateup_mfma", s) != hipSuccess) return MOE_ERR_HIP;
+  } else if (mark(launch_gateup(g, s), "routed_gateup", s) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
   if (shared) {
     DownArgs dn{to_qmat(shared->down), h_sh, T, k, 1, nullptr, nullptr, 1, y_sh};
     if (mark(launch_down(dn, s), "shared_down", s) != hipSuccess) return MOE_ERR_HIP;
   }
   DownArgs dn{to_qmat(routed.down), h, T, k, E, offsets, perm, 0, y_slot};
+  if (mfma) return hip_status(mark(launch_mfma_down(dn, s), "routed_down_mfma", s));
   return hip_status(mark(launch_down(dn, s), "routed_down", s));
 }
 

@@ -60,6 +60,11 @@ struct DownArgs {
 };
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
+// Experts (MFMA grouped GEMM path: many tokens per expert, MXFP4) ------------
+bool mfma_supported(const QMat& gate, const QMat& down);
+hipError_t launch_mfma_gateup(const GateUpArgs& a, hipStream_t s);
+hipError_t launch_mfma_down(const DownArgs& a, hipStream_t s);
+
 // Fused small-batch path (T <= 4 tokens, top-k routing) ------------------------
 struct DecodeArgs {
   const uint16_t* x;       // bf16 [T][d]
