@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
     p.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run an elementwise copy of MIB MiB a few times (scale for HBM byte counters)")
     return p.parse_args()
 
 
@@ -151,6 +153,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 3}))
+        return
 
     import quantized_sparse_moe_amd as qm
     import synth

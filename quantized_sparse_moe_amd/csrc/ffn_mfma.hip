@@ -4,12 +4,14 @@
 // per 32 inputs, the native expert format named on "DeepSeek-V4-Flash-MLX-4bit",
 // which "DeepSeek-V4-Flash-0731-MLX-Serve-mixed-2-3-8bit" notes is exact in bf16).
 //
-// Tiles. A workgroup of 4 waves (2 x 2) owns 128 bucketed tokens of one
-// expert and 64 output rows (gate/up: the same 64 rows of both matrices, so
-// the SwiGLU epilogue has g and u in the same lane) or 128 output rows
-// (down). Each wave: 64 tokens x 32 rows of gate and up (or 64 rows of down)
-// = 16 accumulator tiles of V_MFMA_F32_16X16X32_BF16, small enough for two
-// workgroups per CU.
+// Tiles. A workgroup of 4 waves owns 128 bucketed tokens of one expert and
+// 64 output rows of gate and the same 64 rows of up (so the SwiGLU epilogue
+// has g and u in the same lane), or 128 output rows of down. Each wave takes
+// all 128 tokens and its own 32 columns (16 rows of gate + 16 of up, or 32
+// rows of down): 16 accumulator tiles of V_MFMA_F32_16X16X32_BF16. Every
+// weight fragment a wave converts to bf16 then feeds up to 8 MFMAs, and no
+// two waves convert the same weights; the conversion, not the MFMA, is what
+// bounds a layout in which fragments are reused less.
 //
 // K is consumed 128 at a time. The activations of the tile (gathered through
 // perm for gate/up; contiguous bucketed h rows for down) are staged in LDS,
@@ -31,6 +33,7 @@
 // weights run on the same L2. M-blocks of 16 past the bucket's end skip their
 // MFMAs.
 #include <algorithm>
+#include <type_traits>
 
 #include "ffn_core.hpp"
 
@@ -43,7 +46,8 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // plain 16-byte 
 constexpr int kMT = 128;                 // tokens per workgroup tile
 constexpr int kKT = 128;                 // inputs per K step
 constexpr int kALdsStride = kKT + 8;     // bf16 elements per LDS row (272 bytes)
-constexpr int kRB = 4;                   // 16-row blocks per wave
+constexpr int kRB = 2;                   // 16-column blocks per wave
+constexpr int kMB = kMT / 16;            // 16-token blocks per wave
 
 struct MfmaArgs {
   QMat m0, m1;             // gate, up (GATEUP) or down
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kMT][kALdsStride];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wn = wave;
   const int n = a.T * a.k;
   const QMat& q0 = a.m0;
   const int rows = q0.rows, cols = q0.cols;
@@ -126,41 +130,40 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   }
   __syncthreads();
 
-  // A staging: thread -> (token row tid / 2, half tid % 2 of the 128 inputs)
-  const int a_row = tid >> 1, a_half = tid & 1;
-  const uint16_t* a_src = a.x + static_cast<size_t>(s_src[a_row]) * cols + a_half * 64;
-  u32x4_t a_reg[8];
-  auto load_a = [&](int k0) {
-    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(a_src + k0);
+  // A staging: in round i (0..7) thread t copies 16 bytes, chunk t % 16 of
+  // token row t / 16 + 16 i, so 16 consecutive lanes read one row's 256
+  // contiguous bytes of the K step.
+  const int a_chunk = tid & 15, a_row0 = tid >> 4;
+  uint32_t a_off[8];  // element offsets of this thread's 8 rows (+ its chunk)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a_reg[i] = p[i];
+  for (int i = 0; i < 8; ++i) a_off[i] = static_cast<uint32_t>(s_src[a_row0 + 16 * i]) * cols + a_chunk * 8;
+  auto load_a = [&](u32x4_t (&ar)[8], int k0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ar[i] = *reinterpret_cast<const u32x4_t*>(a.x + a_off[i] + k0);
   };
-  auto store_a = [&](int buf) {
-    u32x4_t* p = reinterpret_cast<u32x4_t*>(&s_a[buf][a_row][a_half * 64]);
+  auto store_a = [&](const u32x4_t (&ar)[8], int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p[i] = a_reg[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row0 + 16 * i][a_chunk * 8]) = ar[i];
   };
 
-  // B: this wave's 4 row blocks (gate/up: 2 of gate + the same 2 of up)
+  // B: this wave's 2 column blocks (gate/up: 16 rows of gate + the same 16 of up)
   const QMat w0 = expert_slice(a.m0, e);
   const QMat w1 = expert_slice(a.m1, e);
   const int g = lane >> 4, r16 = lane & 15;
-  const int row0 = ntile * NTILE + wn * (GATEUP ? 32 : 64) + r16;  // row of block 0 for this lane
+  const int row0 = ntile * NTILE + wn * (GATEUP ? 16 : 32) + r16;  // row of block 0 for this lane
   const size_t rw = static_cast<size_t>(w0.row_words), rg = static_cast<size_t>(w0.row_groups);
   // byte addresses of this lane's rows: block rb is row0 + 16 rb (down) or
-  // row0 + 16 (rb & 1) of gate (rb < 2) / up (rb >= 2)
+  // row0 of gate (rb = 0) / up (rb = 1)
   const uint8_t* c0 = reinterpret_cast<const uint8_t*>(w0.codes) + (static_cast<size_t>(row0) * rw + 4 * g) * 4;
   const uint8_t* c1 = reinterpret_cast<const uint8_t*>(w1.codes) + (static_cast<size_t>(row0) * rw + 4 * g) * 4;
   const uint8_t* e0p = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(row0) * rg + g;
   const uint8_t* e1p = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(row0) * rg + g;
   const size_t cstep = 16 * rw * 4, estep = 16 * rg;
-  u32x4_t b_cur[kRB], b_nxt[kRB];
-  uint32_t s_cur[kRB], s_nxt[kRB];
   auto load_b = [&](u32x4_t (&bv)[kRB], uint32_t (&sv)[kRB], int k0) {
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      const bool second = GATEUP && rb >= 2;
-      const int blk = GATEUP ? (rb & 1) : rb;
+      const bool second = GATEUP && rb == 1;
+      const int blk = GATEUP ? 0 : rb;
       const uint8_t* cp = (second ? c1 : c0) + blk * cstep + k0 / 2;
       const uint8_t* ep = (second ? e1p : e0p) + blk * estep + k0 / 32;
       bv[rb] = *reinterpret_cast<const u32x4_t*>(cp);
@@ -168,61 +171,81 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
     }
   };
 
-  f32x4_t acc[4][kRB];
+  f32x4_t acc[kMB][kRB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kMB; ++i)
 #pragma unroll
     for (int j = 0; j < kRB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int valid_mb = min(4, max(0, (count - wm * 64 + 15) / 16));
+  // the K loop, specialised on the number of 16-token blocks that hold
+  // tokens, so that no MFMA sits behind a branch
+  const int valid_mb = min(kMB, (count + 15) / 16);
   const int nsteps = cols / kKT;
-  load_a(0);
-  load_b(b_cur, s_cur, 0);
-  store_a(0);
-  __syncthreads();
-  for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    const bool more = ks + 1 < nsteps;
-    const int k_next = more ? (ks + 1) * kKT : ks * kKT;
-    load_a(k_next);
-    load_b(b_nxt, s_nxt, k_next);
+  // Software pipeline over K steps: during step ks the activations of step
+  // ks + 2 and the weights of step ks + 1 are in flight, the activations of
+  // step ks + 1 (already in registers) go to the other LDS buffer at the end.
+  // Register sets alternate between even and odd steps (loop unrolled by 2).
+  u32x4_t a_reg0[8], a_reg1[8];
+  u32x4_t b_reg0[kRB], b_reg1[kRB];
+  uint32_t e_reg0[kRB], e_reg1[kRB];
+  auto kloop = [&](auto nmb_tag) {
+    constexpr int NMB = decltype(nmb_tag)::value;
+    auto step = [&](int ks, u32x4_t (&a_ld)[8], const u32x4_t (&a_st)[8], const u32x4_t (&b_use)[kRB],
+                    const uint32_t (&e_use)[kRB], u32x4_t (&b_ld)[kRB], uint32_t (&e_ld)[kRB]) {
+      const int buf = ks & 1;
+      load_a(a_ld, min(ks + 2, nsteps - 1) * kKT);
+      load_b(b_ld, e_ld, min(ks + 1, nsteps - 1) * kKT);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t af[4];
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t af[NMB > 0 ? NMB : 1];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][wm * 64 + mb * 16 + r16][32 * g + 8 * s]);
+        for (int mb = 0; mb < NMB; ++mb)
+          af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][mb * 16 + r16][32 * g + 8 * s]);
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) {
-        const uint32_t word = b_cur[rb][s];
-        const bf16x8_t bf = fp4_to_bf16x8(word, e8m0_to_f32(s_cur[rb]));
+        for (int rb = 0; rb < kRB; ++rb) {
+          if constexpr (NMB > 0) {
+            const bf16x8_t bf = fp4_to_bf16x8(b_use[rb][s], e8m0_to_f32(e_use[rb]));
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          if (mb < valid_mb) acc[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf, acc[mb][rb], 0, 0, 0);
+            for (int mb = 0; mb < NMB; ++mb)
+              acc[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], bf, acc[mb][rb], 0, 0, 0);
+          }
+        }
       }
-    }
-    if (more) store_a(buf ^ 1);
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      b_cur[rb] = b_nxt[rb];
-      s_cur[rb] = s_nxt[rb];
-    }
+      if (ks + 1 < nsteps) store_a(a_st, buf ^ 1);
+      __syncthreads();
+    };
+    load_a(a_reg0, 0);
+    load_b(b_reg0, e_reg0, 0);
+    store_a(a_reg0, 0);
+    load_a(a_reg0, min(1, nsteps - 1) * kKT);
     __syncthreads();
+    for (int ks = 0; ks < nsteps; ks += 2) {
+      step(ks, a_reg1, a_reg0, b_reg0, e_reg0, b_reg1, e_reg1);
+      if (ks + 1 < nsteps) step(ks + 1, a_reg0, a_reg1, b_reg1, e_reg1, b_reg0, e_reg0);
+    }
+  };
+  switch (valid_mb) {
+    case 8: kloop(std::integral_constant<int, 8>{}); break;
+    case 7: kloop(std::integral_constant<int, 7>{}); break;
+    case 6: kloop(std::integral_constant<int, 6>{}); break;
+    case 5: kloop(std::integral_constant<int, 5>{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    default: kloop(std::integral_constant<int, 1>{}); break;
   }
 
   // epilogue: lane holds rows 4 * g + i (tokens) of column r16 (output row)
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < kMB; ++mb) {
     if (mb >= valid_mb) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tl = wm * 64 + mb * 16 + 4 * g + i;
+      const int tl = mb * 16 + 4 * g + i;
       if (tl >= count) continue;
       if constexpr (GATEUP) {
-        uint16_t* hrow = a.h + static_cast<size_t>(p0 + tl) * rows + row0;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          hrow[rb * 16] = static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][rb][i]) * acc[mb][rb + 2][i]));
+        a.h[static_cast<size_t>(p0 + tl) * rows + row0] =
+            static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][0][i]) * acc[mb][1][i]));
       } else {
         const int slot = min(max(a.perm[p0 + tl], 0), n - 1);
         float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
@@ -234,7 +257,9 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-bool mfma_supported(const QMat& gate, const QMat& down) {
+bool mfma_supported(const QMat& gate, const QMat& down, int64_t T, int k) {
+  // activation rows are addressed with 32-bit element offsets
+  if (T * k * std::max(gate.cols, down.cols) >= (int64_t{1} << 31)) return false;
   return gate.fmt == 1 && down.fmt == 1 && gate.cols % kKT == 0 && down.cols % kKT == 0 && gate.rows % 64 == 0 &&
          down.rows % 128 == 0;
 }

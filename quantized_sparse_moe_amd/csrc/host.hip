@@ -6,7 +6,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/qsmoe.h"
+#include "qsmoe.h"
 #include "kernels.hpp"
 
 using namespace qsmoe;
@@ -196,7 +196,7 @@ moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const u
     if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) return MOE_ERR_HIP;
   }
   // Grouped GEMM on the matrix cores once buckets average 16+ tokens.
-  const bool mfma = mfma_supported(to_qmat(routed.gate), to_qmat(routed.down)) &&
+  const bool mfma = mfma_supported(to_qmat(routed.gate), to_qmat(routed.down), T, k) &&
                     static_cast<int64_t>(T) * k >= 16LL * E;
   GateUpArgs g{to_qmat(routed.gate), to_qmat(routed.up), x, T, k, E, offsets, perm, 0, h};
   if (mfma) {

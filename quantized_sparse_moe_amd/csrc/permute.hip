@@ -1,5 +1,5 @@
 // Bucketing of the T*k (token, slot) assignments by expert: a stable counting
-// sort in one workgroup of 8 waves.
+// sort in one workgroup of 16 waves.
 //
 // The stacked expert tensors (mlx-lm PR "Add DeepSeek-v4 (Flash/Pro)",
 // pre-stacked switch_mlp.{gate,up,down}_proj) are run over contiguous buckets
@@ -10,13 +10,16 @@
 // lowest lane is its leader. Pass 1 counts per (wave, expert) in LDS; a scan
 // over (expert, wave) gives every wave its base per expert; pass 2 writes
 // perm[base + rank-within-group] and advances the base. Order within a bucket
-// is ascending assignment index, i.e. the sort is stable.
+// is ascending assignment index, i.e. the sort is stable. Each lane loads the
+// ids of kPermBatch consecutive 64-wide rows at once, so one memory latency is
+// paid per batch rather than per row.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qsmoe {
 
-constexpr int kPermWaves = 8;
+constexpr int kPermWaves = 16;
+constexpr int kPermBatch = 8;
 
 __device__ __forceinline__ uint64_t same_id_mask(bool valid, int id, int nbits) {
   uint64_t m = __ballot(valid);
@@ -44,16 +47,25 @@ __global__ __launch_bounds__(kPermWaves * 64) void k_permute(const int32_t* __re
   const uint64_t lt_mask = (1ull << lane) - 1ull;
 
   // pass 1: per-wave histogram
-  for (int base = s0; base < s1; base += 64) {
-    const int a = base + lane;
-    const bool valid = a < s1;
-    int id = valid ? ids[a] : 0;
-    if (valid && (id < 0 || id >= E)) {
-      set_device_error(err, 4);
-      id = 0;
+  for (int base = s0; base < s1; base += 64 * kPermBatch) {
+    int idv[kPermBatch];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int a = base + u * 64 + lane;
+      idv[u] = a < s1 ? ids[a] : 0;
     }
-    const uint64_t m = same_id_mask(valid, id, nbits);
-    if (valid && (m & lt_mask) == 0) hist[w * E + id] += __popcll(m);
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int a = base + u * 64 + lane;
+      const bool valid = a < s1;
+      int id = idv[u];
+      if (valid && (id < 0 || id >= E)) {
+        set_device_error(err, 4);
+        id = 0;
+      }
+      const uint64_t m = same_id_mask(valid, id, nbits);
+      if (valid && (m & lt_mask) == 0) hist[w * E + id] += __popcll(m);
+    }
   }
   __syncthreads();
 
@@ -95,17 +107,26 @@ __global__ __launch_bounds__(kPermWaves * 64) void k_permute(const int32_t* __re
   __syncthreads();
 
   // pass 2: stable scatter
-  for (int base = s0; base < s1; base += 64) {
-    const int a = base + lane;
-    const bool valid = a < s1;
-    int id = valid ? ids[a] : 0;
-    if (id < 0 || id >= E) id = 0;
-    const uint64_t m = same_id_mask(valid, id, nbits);
-    if (valid) {
-      const int pos = hist[w * E + id] + __popcll(m & lt_mask);
-      perm[pos] = a;
+  for (int base = s0; base < s1; base += 64 * kPermBatch) {
+    int idv[kPermBatch];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int a = base + u * 64 + lane;
+      idv[u] = a < s1 ? ids[a] : 0;
     }
-    if (valid && (m & lt_mask) == 0) hist[w * E + id] += __popcll(m);
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const int a = base + u * 64 + lane;
+      const bool valid = a < s1;
+      int id = idv[u];
+      if (id < 0 || id >= E) id = 0;
+      const uint64_t m = same_id_mask(valid, id, nbits);
+      if (valid) {
+        const int pos = hist[w * E + id] + __popcll(m & lt_mask);
+        perm[pos] = a;
+      }
+      if (valid && (m & lt_mask) == 0) hist[w * E + id] += __popcll(m);
+    }
   }
 }
 
@@ -114,6 +135,10 @@ hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* offsets, in
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const size_t lds = (static_cast<size_t>(kPermWaves) * E + kPermWaves) * sizeof(int32_t);
+  // up to 1024 experts needs a little over the default 64 KiB of dynamic LDS
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_permute),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermWaves * 64), lds, s, ids, n, E, nbits, offsets, perm, err);
   return hipGetLastError();
 }

@@ -22,61 +22,120 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Logits, many tokens: 64 tokens x 64 experts per workgroup, K step 32 staged
-// through LDS in fp32, 4x4 outputs per thread. Requires d % 32 == 0.
+// Logits, many tokens: MFMA with the fp32 gate split into three bf16 terms.
+//
+// Truncating w to its top 16 bits gives hi (exact bf16); the remainder w - hi
+// is exact in fp32 and carries at most 16 significant bits, so a second
+// truncation gives mid and a third remainder lo that is itself exact in bf16
+// (8 + 8 + 8 bits cover fp32's 24-bit significand). Every x*hi, x*mid, x*lo
+// product of two bf16 values is exact in fp32, so three bf16 MFMAs with fp32
+// accumulation give x.w to fp32 accumulation error, as an fp32 dot product
+// would, at bf16 matrix-core rate.
+//
+// Workgroup: MB*16 tokens x 64 experts; its four waves each take every fourth
+// 32-wide K step over the whole tile and the partial tiles are added in wave
+// order through LDS, so the result does not depend on timing. Fragments are
+// loaded straight from global memory in the V_MFMA_F32_16X16X32_BF16 operand
+// layout (lane l: row l % 16, inputs 8 (l / 16) .. + 7 of the step).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_logits_tiled(const uint16_t* __restrict__ x, const float* __restrict__ wr,
-                                                      int T, int E, int d, float* __restrict__ logits) {
-  __shared__ float xs[32][64 + 4];
-  __shared__ float ws[32][64 + 4];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
-  const int tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
-  const int lr = tid >> 2, lc = (tid & 3) * 8;  // loader: row (token / expert), 8 columns
-  const int lt = min(t0 + lr, T - 1), le = min(e0 + lr, E - 1);
-  for (int k0 = 0; k0 < d; k0 += 32) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(lt) * d + k0 + lc);
-    const float4 w0 = *reinterpret_cast<const float4*>(wr + static_cast<size_t>(le) * d + k0 + lc);
-    const float4 w1 = *reinterpret_cast<const float4*>(wr + static_cast<size_t>(le) * d + k0 + lc + 4);
-    __syncthreads();
-    xs[lc + 0][lr] = bf16_to_f32(xv.x & 0xffffu);
-    xs[lc + 1][lr] = bf16_to_f32(xv.x >> 16);
-    xs[lc + 2][lr] = bf16_to_f32(xv.y & 0xffffu);
-    xs[lc + 3][lr] = bf16_to_f32(xv.y >> 16);
-    xs[lc + 4][lr] = bf16_to_f32(xv.z & 0xffffu);
-    xs[lc + 5][lr] = bf16_to_f32(xv.z >> 16);
-    xs[lc + 6][lr] = bf16_to_f32(xv.w & 0xffffu);
-    xs[lc + 7][lr] = bf16_to_f32(xv.w >> 16);
-    ws[lc + 0][lr] = w0.x;
-    ws[lc + 1][lr] = w0.y;
-    ws[lc + 2][lr] = w0.z;
-    ws[lc + 3][lr] = w0.w;
-    ws[lc + 4][lr] = w1.x;
-    ws[lc + 5][lr] = w1.y;
-    ws[lc + 6][lr] = w1.z;
-    ws[lc + 7][lr] = w1.w;
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(&xs[kk][ty * 4]);
-      const float4 b = *reinterpret_cast<const float4*>(&ws[kk][tx * 4]);
-      const float av[4] = {a.x, a.y, a.z, a.w};
-      const float bv[4] = {b.x, b.y, b.z, b.w};
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+__device__ __forceinline__ void split3_bf16x8(const u32x4_t& w0, const u32x4_t& w1, bf16x8_t& hi, bf16x8_t& mid,
+                                              bf16x8_t& lo) {
+  uint32_t h[4], m[4], l[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t bits = j < 4 ? w0[j] : w1[j - 4];
+    const uint32_t hb = bits & 0xffff0000u;
+    const float r1 = __uint_as_float(bits) - __uint_as_float(hb);
+    const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(mb);
+    const uint32_t lb = __float_as_uint(r2) >> 16;  // exact: r2 has at most 8 significant bits
+    if (j & 1) {
+      h[j >> 1] |= hb;
+      m[j >> 1] |= mb;
+      l[j >> 1] |= lb << 16;
+    } else {
+      h[j >> 1] = hb >> 16;
+      m[j >> 1] = mb >> 16;
+      l[j >> 1] = lb;
     }
   }
+  hi = __builtin_bit_cast(bf16x8_t, h);
+  mid = __builtin_bit_cast(bf16x8_t, m);
+  lo = __builtin_bit_cast(bf16x8_t, l);
+}
+
+template <int MB>
+__global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict__ x, const float* __restrict__ wr,
+                                                     int T, int E, int d, float* __restrict__ logits) {
+  constexpr int NB = 4;  // 16-expert blocks per workgroup
+  __shared__ f32x4_t s_part[3][MB * NB][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int t0 = blockIdx.y * (MB * 16), e0 = blockIdx.x * (NB * 16);
+  const uint16_t* xa[MB];
+  const float* wb[NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
+  for (int mb = 0; mb < MB; ++mb) xa[mb] = x + static_cast<size_t>(min(t0 + mb * 16 + r16, T - 1)) * d + 8 * g;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) logits[static_cast<size_t>(t) * E + e] = acc[i][j];
+  for (int nb = 0; nb < NB; ++nb) wb[nb] = wr + static_cast<size_t>(min(e0 + nb * 16 + r16, E - 1)) * d + 8 * g;
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = d / 32;
+  for (int ks = wave; ks < nsteps; ks += 4) {
+    const int k0 = ks * 32;
+    bf16x8_t af[MB];
+    u32x4_t bw[NB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const bf16x8_t*>(xa[mb] + k0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bw[nb][0] = *reinterpret_cast<const u32x4_t*>(wb[nb] + k0);
+      bw[nb][1] = *reinterpret_cast<const u32x4_t*>(wb[nb] + k0 + 4);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      bf16x8_t hi, mid, lo;
+      split3_bf16x8(bw[nb][0], bw[nb][1], hi, mid, lo);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], lo, acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], mid, acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb], hi, acc[mb][nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // fixed-order reduction of the four waves' partial tiles
+  if (wave > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s_part[wave - 1][mb * NB + nb][lane] = acc[mb][nb];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      f32x4_t v = acc[mb][nb];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) v += s_part[w][mb * NB + nb][lane];
+      const int e = e0 + nb * 16 + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + mb * 16 + 4 * g + i;
+        if (t < T && e < E) logits[static_cast<size_t>(t) * E + e] = v[i];
+      }
     }
   }
 }
@@ -191,9 +250,12 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
 // ---------------------------------------------------------------------------
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E, int d, float* logits,
                                 hipStream_t s) {
-  if (T > 16) {
-    dim3 grid((E + 63) / 64, (T + 63) / 64);
-    hipLaunchKernelGGL(k_logits_tiled, grid, dim3(256), 0, s, x, wr, T, E, d, logits);
+  if (T > 256) {
+    hipLaunchKernelGGL(k_logits_mfma<4>, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, wr, T, E, d,
+                       logits);
+  } else if (T > 16) {
+    hipLaunchKernelGGL(k_logits_mfma<1>, dim3((E + 63) / 64, (T + 15) / 16), dim3(256), 0, s, x, wr, T, E, d,
+                       logits);
   } else if (T == 1) {
     hipLaunchKernelGGL(k_logits_gemv<1>, dim3((E + 3) / 4, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else if (T == 2) {
