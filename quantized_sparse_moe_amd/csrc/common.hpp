@@ -37,6 +37,14 @@ __device__ __forceinline__ float sqrtsoftplus(float l) {
   return sqrtf(fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l))));
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads issued
+// before it stay in flight (a plain __syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

@@ -68,28 +68,28 @@ __device__ __forceinline__ bf16x8_t fp4_to_bf16x8(uint32_t word, float scale) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
-  constexpr int NTILE = GATEUP ? 64 : 128;    // output rows per workgroup (per matrix)
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int32_t s_mt[kMaxExperts + 1];
-  __shared__ int32_t s_src[kMT];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kMT][kALdsStride];
+// Which (expert m-tile, n-tile) pair this workgroup computes. Tiles are MT
+// bucketed tokens of one expert; an expert with c tokens has ceil(c / MT)
+// m-tiles, counted from expert_offsets with a wave scan (staged in LDS).
+// Pairs are dealt to the 8 XCDs in contiguous runs (blockIdx % 8 picks the
+// XCD), so the workgroups sharing an m-tile's activations and an expert's
+// weights run on the same L2. Returns false (for the whole workgroup) when
+// the grid's upper bound left this workgroup without a pair.
+struct Tile {
+  int e, p0, count, ntile;
+};
 
+template <int MT>
+__device__ bool tile_of_block(const MfmaArgs& a, int n_ntiles, int32_t* s_off, int32_t* s_mt, Tile& t) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int wn = wave;
   const int n = a.T * a.k;
-  const QMat& q0 = a.m0;
-  const int rows = q0.rows, cols = q0.cols;
-
-  // m-tiles per expert (exclusive scan of ceil(count / kMT))
   for (int i = tid; i <= a.E; i += 256) s_off[i] = min(max(a.offsets[i], 0), n);
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
     for (int e0 = 0; e0 < a.E; e0 += 64) {
       const int e = e0 + lane;
-      const int c = e < a.E ? (max(s_off[e + 1] - s_off[e], 0) + kMT - 1) / kMT : 0;
+      const int c = e < a.E ? (max(s_off[e + 1] - s_off[e], 0) + MT - 1) / MT : 0;
       int incl = c;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -102,16 +102,14 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
     if (lane == 0) s_mt[a.E] = carry;
   }
   __syncthreads();
-  const int n_ntiles = rows / NTILE;
   const int64_t pairs = static_cast<int64_t>(s_mt[a.E]) * n_ntiles;
   const int64_t per_xcd = (pairs + 7) / 8;
   const int64_t local = blockIdx.x / 8;
-  if (local >= per_xcd) return;
+  if (local >= per_xcd) return false;
   const int64_t pair = (blockIdx.x % 8) * per_xcd + local;
-  if (pair >= pairs) return;
-  const int mtile = static_cast<int>(pair / n_ntiles), ntile = static_cast<int>(pair % n_ntiles);
-
-  // expert of this m-tile
+  if (pair >= pairs) return false;
+  const int mtile = static_cast<int>(pair / n_ntiles);
+  t.ntile = static_cast<int>(pair % n_ntiles);
   int e = 0;
   for (int e0 = 0; e0 < a.E; e0 += 64) {
     const int ee = e0 + lane;
@@ -122,8 +120,27 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
       break;
     }
   }
-  const int p0 = s_off[e] + (mtile - s_mt[e]) * kMT;
-  const int count = min(kMT, s_off[e + 1] - p0);
+  t.e = e;
+  t.p0 = s_off[e] + (mtile - s_mt[e]) * MT;
+  t.count = min(MT, s_off[e + 1] - t.p0);
+  return true;
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
+  constexpr int NTILE = GATEUP ? 64 : 128;    // output rows per workgroup (per matrix)
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int32_t s_mt[kMaxExperts + 1];
+  __shared__ int32_t s_src[kMT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kMT][kALdsStride];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wn = wave;
+  const int n = a.T * a.k;
+  const int rows = a.m0.rows, cols = a.m0.cols;
+  Tile t;
+  if (!tile_of_block<kMT>(a, rows / NTILE, s_off, s_mt, t)) return;
+  const int e = t.e, p0 = t.p0, count = t.count, ntile = t.ntile;
   if (tid < kMT) {
     const int p = p0 + min(tid, count - 1);
     s_src[tid] = GATEUP ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
@@ -211,18 +228,20 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
           }
         }
       }
-      if (ks + 1 < nsteps) store_a(a_st, buf ^ 1);
-      __syncthreads();
+      store_a(a_st, buf ^ 1);  // after the last step: unused, harmless
+      lds_barrier();
     };
     load_a(a_reg0, 0);
     load_b(b_reg0, e_reg0, 0);
     store_a(a_reg0, 0);
     load_a(a_reg0, min(1, nsteps - 1) * kKT);
-    __syncthreads();
-    for (int ks = 0; ks < nsteps; ks += 2) {
+    lds_barrier();
+    int ks = 0;
+    for (; ks + 2 <= nsteps; ks += 2) {
       step(ks, a_reg1, a_reg0, b_reg0, e_reg0, b_reg1, e_reg1);
-      if (ks + 1 < nsteps) step(ks + 1, a_reg0, a_reg1, b_reg1, e_reg1, b_reg0, e_reg0);
+      step(ks + 1, a_reg0, a_reg1, b_reg1, e_reg1, b_reg0, e_reg0);
     }
+    if (ks < nsteps) step(ks, a_reg1, a_reg0, b_reg0, e_reg0, b_reg1, e_reg1);
   };
   switch (valid_mb) {
     case 8: kloop(std::integral_constant<int, 8>{}); break;
@@ -257,30 +276,338 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Affine 4-bit experts (w = s q + b per group of G inputs, fp16 s and b).
+//
+// Codes become exact bf16 without a multiply: the bits 0x4300 | q are the
+// value 128 + q. Each MFMA pass covers 32 consecutive inputs, so all of them
+// lie in one group per output row, and per group the kernel gets
+//   D[m][n] = sum_k x[m][k] (128 + q[n][k])   and   X[m] = sum_k x[m][k]
+// (X from an extra MFMA against a B operand of ones), then adds
+//   s[n] D[m][n] + (b[n] - 128 s[n]) X[m]
+// = sum_k x[m][k] (s[n] q[n][k] + b[n]) to the fp32 accumulator: exact
+// products, fp32 sums, the group's scale and bias applied once per group.
+//
+// This layout serves buckets of a few tokens (hash routing, mid-size
+// batches), where the weight stream is the cost. Tiles: MT (16 or 32)
+// bucketed tokens x RB * 16 columns per wave (gate/up: RB/2 blocks of gate
+// and the same rows of up), 4 waves per workgroup. Lane group g of pass s
+// holds inputs 32 s + 8 g .. + 7; each lane loads 16 contiguous bytes of its
+// row (inputs 32 g .. + 31) and the words are transposed across the lane
+// groups through the wave's own LDS slot. Scales and biases are fetched once
+// per 4 K steps (lane group j holds step j's) and broadcast with a lane
+// shuffle. The 8 codes of one word decode to bf16 in the order
+// (0, 4, 1, 5, 2, 6, 3, 7) with one and-or per pair; the activations are
+// stored to LDS in that same order within each 8-input chunk.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4_t interleave_halves(const u32x4_t& v) {
+  // (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
+  return u32x4_t{(v[0] & 0xffffu) | (v[2] << 16), (v[0] >> 16) | (v[2] & 0xffff0000u),
+                 (v[1] & 0xffffu) | (v[3] << 16), (v[1] >> 16) | (v[3] & 0xffff0000u)};
+}
+
+__device__ __forceinline__ bf16x8_t u4_to_bf16x8_offset128(uint32_t w) {
+  const u32x4_t r{(w & 0x000f000fu) | 0x43004300u, ((w >> 4) & 0x000f000fu) | 0x43004300u,
+                  ((w >> 8) & 0x000f000fu) | 0x43004300u, ((w >> 12) & 0x000f000fu) | 0x43004300u};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
+
+template <int G>
+struct AffScaleWords {
+  // packed fp16 words per row per K step: scales (and as many for biases)
+  static constexpr int GPS = kKT / G;
+  static constexpr int W = (GPS + 1) / 2;
+};
+
+template <bool GATEUP, int G, int MT>
+__global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
+  constexpr int RB = kAffRB;
+  constexpr int HB = GATEUP ? RB / 2 : RB;           // row blocks per matrix per wave
+  constexpr int NTILE = 4 * HB * 16;                 // rows per matrix per workgroup
+  constexpr int PPG = G / 32;                        // MFMA passes per group
+  constexpr int GPS = kKT / G;                       // groups per K step
+  constexpr int SW = AffScaleWords<G>::W;            // scale words per row per step
+  constexpr int MB = MT / 16;
+  constexpr int ACH = (MT * 16 + 255) / 256;         // 16-byte activation chunks per thread per step
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ int32_t s_mt[kMaxExperts + 1];
+  __shared__ int32_t s_src[MT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
+  __shared__ __attribute__((aligned(16))) uint32_t s_bt[4][RB][4][16][4];  // per wave: [rb][block][row][word]
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int n = a.T * a.k;
+  const int rows = a.m0.rows, cols = a.m0.cols;
+  Tile t;
+  if (!tile_of_block<MT>(a, rows / NTILE, s_off, s_mt, t)) return;
+  const int e = t.e, p0 = t.p0, count = t.count, ntile = t.ntile;
+  if (tid < MT) {
+    const int p = p0 + min(tid, count - 1);
+    s_src[tid] = GATEUP ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
+  }
+  __syncthreads();
+
+  // activations: round i, thread t copies chunk t % 16 of row t / 16 + 16 i
+  // (threads beyond the tile's rows repeat the last row's copy)
+  const int a_chunk = tid & 15;
+  int a_row[ACH];
+  uint32_t a_off[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    a_row[i] = min((tid >> 4) + 16 * i, MT - 1);
+    a_off[i] = static_cast<uint32_t>(s_src[a_row[i]]) * cols + a_chunk * 8;
+  }
+  auto load_a = [&](u32x4_t (&ar)[ACH], int k0) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) ar[i] = *reinterpret_cast<const u32x4_t*>(a.x + a_off[i] + k0);
+  };
+  auto store_a = [&](const u32x4_t (&ar)[ACH], int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+      *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row[i]][a_chunk * 8]) = interleave_halves(ar[i]);
+  };
+
+  // weights: lane (g, r16) of block rb reads 16 bytes (inputs 32 g .. + 31)
+  // of row rbase + 16 (rb % HB) + r16 of gate (rb < HB) or up (rb >= HB)
+  const QMat w0 = expert_slice(a.m0, e);
+  const QMat w1 = expert_slice(a.m1, e);
+  const int g = lane >> 4, r16 = lane & 15;
+  const int rbase = ntile * NTILE + wave * HB * 16 + r16;
+  const size_t rw = static_cast<size_t>(w0.row_words), rg = static_cast<size_t>(w0.row_groups);
+  const uint32_t* c0 = w0.codes + static_cast<size_t>(rbase) * rw + 4 * g;
+  const uint32_t* c1 = w1.codes + static_cast<size_t>(rbase) * rw + 4 * g;
+  const uint16_t* s0p = static_cast<const uint16_t*>(w0.scales) + static_cast<size_t>(rbase) * rg;
+  const uint16_t* s1p = static_cast<const uint16_t*>(w1.scales) + static_cast<size_t>(rbase) * rg;
+  const uint16_t* b0p = w0.biases + static_cast<size_t>(rbase) * rg;
+  const uint16_t* b1p = w1.biases + static_cast<size_t>(rbase) * rg;
+  const size_t cstep = 16 * rw, gstep = 16 * rg;
+  const int nsteps = cols / kKT;
+
+  auto load_b = [&](u32x4_t (&bq)[RB], int k0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint32_t* cp = (rb >= HB ? c1 : c0) + (rb % HB) * cstep + k0 / 8;
+      bq[rb] = *reinterpret_cast<const u32x4_t*>(cp);
+    }
+  };
+  // scales/biases of K steps ks0 .. ks0 + 3: lane group j holds step ks0 + j's
+  struct Scales {
+    uint32_t s[RB][SW], b[RB][SW];
+  };
+  auto load_scales = [&](Scales& sc, int ks0) {
+    const int kq = min(ks0 + g, nsteps - 1) * GPS;  // first group of this lane's step
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint16_t* sp = (rb >= HB ? s1p : s0p) + (rb % HB) * gstep + kq;
+      const uint16_t* bp = (rb >= HB ? b1p : b0p) + (rb % HB) * gstep + kq;
+      if constexpr (GPS == 1) {
+        sc.s[rb][0] = *sp;
+        sc.b[rb][0] = *bp;
+      } else {
+#pragma unroll
+        for (int j = 0; j < SW; ++j) {
+          sc.s[rb][j] = reinterpret_cast<const uint32_t*>(sp)[j];
+          sc.b[rb][j] = reinterpret_cast<const uint32_t*>(bp)[j];
+        }
+      }
+    }
+  };
+
+  f32x4_t acc[MB][RB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < RB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int valid_mb = min(MB, (count + 15) / 16);
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  u32x4_t a_reg0[ACH], a_reg1[ACH];
+  u32x4_t b_reg0[RB], b_reg1[RB];
+  Scales sc_cur, sc_nxt;
+
+  auto kloop = [&](auto nmb_tag) {
+    constexpr int NMB = decltype(nmb_tag)::value;
+    // step ks = round base + J; weights one step ahead, activations two
+    auto step = [&](int ks, auto j_tag, u32x4_t (&a_ld)[ACH], const u32x4_t (&a_st)[ACH],
+                    const u32x4_t (&b_use)[RB], u32x4_t (&b_ld)[RB]) {
+      constexpr int J = decltype(j_tag)::value;
+      const int buf = ks & 1;
+      load_b(b_ld, min(ks + 1, nsteps - 1) * kKT);
+      load_a(a_ld, min(ks + 2, nsteps - 1) * kKT);
+      if constexpr (J == 0) load_scales(sc_nxt, ks + 4);
+      // transpose the step's code words across the lane groups (own LDS slot)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) *reinterpret_cast<u32x4_t*>(&s_bt[wave][rb][g][r16][0]) = b_use[rb];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      uint32_t qw[RB][4];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qw[rb][s] = s_bt[wave][rb][s][r16][g];
+      // this step's scales and biases live in lane group J
+      uint32_t sw[RB][SW], bw[RB][SW];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int w = 0; w < SW; ++w) {
+          sw[rb][w] = __shfl(sc_cur.s[rb][w], J * 16 + r16);
+          bw[rb][w] = __shfl(sc_cur.b[rb][w], J * 16 + r16);
+        }
+
+      f32x4_t dg[GPS][NMB][RB], xg[GPS][NMB];
+#pragma unroll
+      for (int j = 0; j < GPS; ++j) {
+#pragma unroll
+        for (int pp = 0; pp < PPG; ++pp) {
+          const int s = j * PPG + pp;
+          bf16x8_t af[NMB];
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+            af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][mb * 16 + r16][32 * s + 8 * g]);
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+            xg[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                af[mb], ones, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : xg[j][mb], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            const bf16x8_t bf = u4_to_bf16x8_offset128(qw[rb][s]);
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+              dg[j][mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  af[mb], bf, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : dg[j][mb][rb], 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < GPS; ++j) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float sc = f16_to_f32(static_cast<uint16_t>(sw[rb][j / 2] >> (16 * (j & 1))));
+          const float bc = fmaf(-128.0f, sc, f16_to_f32(static_cast<uint16_t>(bw[rb][j / 2] >> (16 * (j & 1)))));
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[mb][rb][i] = fmaf(sc, dg[j][mb][rb][i], fmaf(bc, xg[j][mb][i], acc[mb][rb][i]));
+        }
+      }
+      if constexpr (J == 3) sc_cur = sc_nxt;
+      store_a(a_st, buf ^ 1);  // after the last step: unused, harmless
+      lds_barrier();
+    };
+    using J0 = std::integral_constant<int, 0>;
+    using J1 = std::integral_constant<int, 1>;
+    using J2 = std::integral_constant<int, 2>;
+    using J3 = std::integral_constant<int, 3>;
+    load_scales(sc_cur, 0);
+    load_b(b_reg0, 0);
+    load_a(a_reg0, 0);
+    store_a(a_reg0, 0);
+    load_a(a_reg0, min(1, nsteps - 1) * kKT);
+    lds_barrier();
+    int ks = 0;
+    for (; ks + 4 <= nsteps; ks += 4) {
+      step(ks, J0{}, a_reg1, a_reg0, b_reg0, b_reg1);
+      step(ks + 1, J1{}, a_reg0, a_reg1, b_reg1, b_reg0);
+      step(ks + 2, J2{}, a_reg1, a_reg0, b_reg0, b_reg1);
+      step(ks + 3, J3{}, a_reg0, a_reg1, b_reg1, b_reg0);
+    }
+    if (ks < nsteps) step(ks, J0{}, a_reg1, a_reg0, b_reg0, b_reg1);
+    if (ks + 1 < nsteps) step(ks + 1, J1{}, a_reg0, a_reg1, b_reg1, b_reg0);
+    if (ks + 2 < nsteps) step(ks + 2, J2{}, a_reg1, a_reg0, b_reg0, b_reg1);
+  };
+  if constexpr (MB == 2) {
+    if (valid_mb == 2)
+      kloop(std::integral_constant<int, 2>{});
+    else
+      kloop(std::integral_constant<int, 1>{});
+  } else {
+    kloop(std::integral_constant<int, 1>{});
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb >= valid_mb) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tl = mb * 16 + 4 * g + i;
+      if (tl >= count) continue;
+      if constexpr (GATEUP) {
+        uint16_t* hrow = a.h + static_cast<size_t>(p0 + tl) * rows + rbase;
+#pragma unroll
+        for (int rb = 0; rb < HB; ++rb)
+          hrow[rb * 16] = static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][rb][i]) * acc[mb][rb + HB][i]));
+      } else {
+        const int slot = min(max(a.perm[p0 + tl], 0), n - 1);
+        float* yrow = a.y + static_cast<size_t>(slot) * rows + rbase;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) yrow[rb * 16] = acc[mb][rb][i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+static bool affine4_mfma_ok(const QMat& m) {
+  return m.fmt == 0 && m.bits == 4 && (m.group == 32 || m.group == 64 || m.group == 128);
+}
+
 bool mfma_supported(const QMat& gate, const QMat& down, int64_t T, int k) {
   // activation rows are addressed with 32-bit element offsets
   if (T * k * std::max(gate.cols, down.cols) >= (int64_t{1} << 31)) return false;
-  return gate.fmt == 1 && down.fmt == 1 && gate.cols % kKT == 0 && down.cols % kKT == 0 && gate.rows % 64 == 0 &&
-         down.rows % 128 == 0;
+  if (gate.fmt == 1 && down.fmt == 1)
+    return gate.cols % kKT == 0 && down.cols % kKT == 0 && gate.rows % 64 == 0 && down.rows % 128 == 0;
+  return affine4_mfma_ok(gate) && affine4_mfma_ok(down) && gate.cols % kKT == 0 && down.cols % kKT == 0 &&
+         gate.rows % (32 * kAffRB) == 0 && down.rows % (64 * kAffRB) == 0;
 }
 
-static unsigned mfma_grid(int T, int k, int E, int rows, int ntile) {
+static unsigned mfma_grid(int T, int k, int E, int rows, int ntile, int mt) {
   const int64_t tk = static_cast<int64_t>(T) * k;
-  const int64_t mtiles = (tk + kMT - 1) / kMT + std::min<int64_t>(tk, E);
+  const int64_t mtiles = (tk + mt - 1) / mt + std::min<int64_t>(tk, E);
   const int64_t pairs = mtiles * (rows / ntile);
   return static_cast<unsigned>(((pairs + 7) / 8) * 8);
 }
 
-hipError_t launch_mfma_gateup(const GateUpArgs& g, hipStream_t s) {
-  MfmaArgs a{g.gate, g.up, g.x, g.T, g.k, g.E, g.offsets, g.perm, g.h, nullptr};
-  hipLaunchKernelGGL((k_mfma_mxfp4<true>), dim3(mfma_grid(g.T, g.k, g.E, g.gate.rows, 64)), dim3(256), 0, s, a);
+template <bool GATEUP, int MT>
+static void launch_affine(const MfmaArgs& a, hipStream_t s) {
+  constexpr int NTILE = (GATEUP ? 32 : 64) * kAffRB;
+  const dim3 grid(mfma_grid(a.T, a.k, a.E, a.m0.rows, NTILE, MT));
+  if constexpr (MT == 16) {
+    if (a.m0.group == 32) {
+      hipLaunchKernelGGL((k_mfma_affine4<GATEUP, 32, 16>), grid, dim3(256), 0, s, a);
+      return;
+    }
+  }
+  if (a.m0.group == 64)
+    hipLaunchKernelGGL((k_mfma_affine4<GATEUP, 64, MT>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_mfma_affine4<GATEUP, 128, MT>), grid, dim3(256), 0, s, a);
+}
+
+template <bool GATEUP>
+static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
+  const QMat& m = a.m0;
+  if (m.fmt == 1) {
+    constexpr int NTILE = GATEUP ? 64 : 128;
+    hipLaunchKernelGGL((k_mfma_mxfp4<GATEUP>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, kMT)), dim3(256), 0, s,
+                       a);
+  } else if (static_cast<int64_t>(a.T) * a.k < 16LL * a.E || m.group == 32) {
+    launch_affine<GATEUP, 16>(a, s);  // buckets average under 16 tokens (or 4 groups per step)
+  } else {
+    launch_affine<GATEUP, 32>(a, s);
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_mfma_gateup(const GateUpArgs& g, hipStream_t s) {
+  return launch_mfma<true>(MfmaArgs{g.gate, g.up, g.x, g.T, g.k, g.E, g.offsets, g.perm, g.h, nullptr}, s);
+}
+
 hipError_t launch_mfma_down(const DownArgs& d, hipStream_t s) {
-  MfmaArgs a{d.down, d.down, d.h, d.T, d.k, d.E, d.offsets, d.perm, nullptr, d.y};
-  hipLaunchKernelGGL((k_mfma_mxfp4<false>), dim3(mfma_grid(d.T, d.k, d.E, d.down.rows, 128)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_mfma<false>(MfmaArgs{d.down, d.down, d.h, d.T, d.k, d.E, d.offsets, d.perm, nullptr, d.y}, s);
 }
 
 }  // namespace qsmoe

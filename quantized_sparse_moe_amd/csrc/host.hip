@@ -195,9 +195,9 @@ moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const u
     GateUpArgs g{to_qmat(shared->gate), to_qmat(shared->up), x, T, k, 1, nullptr, nullptr, 1, h_sh};
     if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) return MOE_ERR_HIP;
   }
-  // Grouped GEMM on the matrix cores once buckets average 16+ tokens.
+  // Grouped GEMM on the matrix cores once buckets average 4+ tokens.
   const bool mfma = mfma_supported(to_qmat(routed.gate), to_qmat(routed.down), T, k) &&
-                    static_cast<int64_t>(T) * k >= 16LL * E;
+                    static_cast<int64_t>(T) * k >= 4LL * E;
   GateUpArgs g{to_qmat(routed.gate), to_qmat(routed.up), x, T, k, E, offsets, perm, 0, h};
   if (mfma) {
     if (mark(launch_mfma_gateup(g, s), "routed_gateup_mfma", s) != hipSuccess) return MOE_ERR_HIP;

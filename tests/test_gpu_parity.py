@@ -33,6 +33,14 @@ SMALL = [
     variant("mixed", "mixed_2x8", 107, T=9, d=4096, I=256, E=16, top_k=4, gate_up=FormatSpec("affine", 8, 64),
             down=FormatSpec("affine", 2, 64), shared=FormatSpec("affine", 3, 32), I_shared=128),
     variant("prefill", "mxfp4_wide", 108, T=33, d=6144, I=128, E=8, top_k=2, bias_kind="normal"),
+    # matrix-core paths: MXFP4 buckets spanning two 128-token tiles; affine
+    # 4-bit buckets spanning several 32-token tiles, groups of 32, 64 and 128
+    variant("prefill", "mxfp4_big_bucket", 112, T=300, d=256, I=128, E=4, top_k=2, bias_kind="normal"),
+    variant("prefill", "aff4_g32_g128_mfma", 113, T=96, d=512, I=256, E=8, top_k=2, bias_kind="normal",
+            gate_up=FormatSpec("affine", 4, 32), down=FormatSpec("affine", 4, 128)),
+    variant("prefill", "aff4_g64_mfma_shared", 114, T=80, d=768, I=384, E=16, top_k=4, bias_kind="normal",
+            gate_up=FormatSpec("affine", 4, 64), down=FormatSpec("affine", 4, 64),
+            shared=FormatSpec("affine", 8, 64), I_shared=128),
 ]
 
 
