@@ -2,7 +2,7 @@
 // eight when a step has at most 4 tokens, top-k routing and at most 256
 // experts.
 //
-//   1. k_dec_router: the fp32 router logits (one wave per expert) with each
+//   1. k_dec_router: the fp32 router logits (one workgroup per expert) with each
 //      expert's score and ranking key, and on the remaining workgroups the
 //      shared expert's gate/up + SwiGLU (no routing needed).
 //   2. k_dec_gateup: each workgroup selects the top-k from the keys (same
@@ -41,15 +41,17 @@ constexpr int kDecMaxT = 4;
 constexpr int kDecMaxK = 8;
 
 
-// Launch 1: router logits of four experts per workgroup (one per wave), with
-// each expert's score and ranking key for every token; the remaining
-// workgroups stream the shared expert's gate/up, which needs no routing.
+// Launch 1: router logits of one expert per workgroup (split-K over its four
+// waves), with the expert's score and ranking key for every token; the
+// remaining workgroups stream the shared expert's gate/up, which needs no
+// routing.
 template <int TT, int SCPL, int SNT>
 __global__ __launch_bounds__(256) void k_dec_router(DecodeArgs a) {
+  __shared__ float s_part[4 * TT];
   QSMOE_TL(0, 0);
   if (static_cast<int>(blockIdx.x) < a.n_logit_blocks) {
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e < a.E) logits_wave<TT>(a.x, a.wr, a.T, a.E, a.d, e, 0, a.logits, a.bias, a.keys, a.scores);
+    logits_wg<TT>(a.x, a.wr, a.T, a.E, a.d, blockIdx.x, 0, a.logits, s_part, a.bias, a.keys, a.scores);
+    QSMOE_TL(0, 1);
   } else if constexpr (SNT > 0) {
     StreamArgs sa{a.sgate, a.sup, a.x, a.T, a.k, 1, nullptr, nullptr, 1, a.h_sh, nullptr};
     ffn_stream_body<0, 8, SCPL, SNT, true>(sa, blockIdx.x - a.n_logit_blocks, gridDim.x - a.n_logit_blocks, nullptr,
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
     const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
     const QMat q0 = expert_slice(a.gate, e), q1 = expert_slice(a.up, e);
     uint16_t* hs = a.h + static_cast<size_t>(slot) * rows;
-    stream_rows<F, B, CPL, 1, true>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
+    stream_rows<F, B, CPL, 1, true, 1>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
                                     [&](int, int r, float g, float up) {
                                       hs[r] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * up));
                                     });
@@ -152,7 +154,7 @@ __device__ __forceinline__ float row_dot_one(const RowRegs<F, B, CPL>& r, const 
   return acc;
 }
 
-constexpr int kDecRows = 2;  // output rows per batch per wave
+constexpr int kDecRows = 1;  // output rows per batch per wave
 
 template <int F, int B, int K, bool SH>
 struct DownBatch {
@@ -322,7 +324,7 @@ static int dec_shared_nt(const DecodeArgs& a, int cpl) {
 
 hipError_t launch_dec_router(const DecodeArgs& a0, hipStream_t s) {
   DecodeArgs a = a0;
-  a.n_logit_blocks = (a.E + 3) / 4;
+  a.n_logit_blocks = a.E;
   const int scpl = a.has_shared ? dec_cpl(a.sgate.cols) : 1;
   const int snt = dec_shared_nt(a, scpl);
   unsigned grid = a.n_logit_blocks;

@@ -285,39 +285,39 @@ struct StreamArgs {
 constexpr int kMaxExperts = 1024;
 
 // Rows [r_begin, r_end) of q0 (and q1) against the activations in xr. Rows
-// go in batches of kBatchRows per wave, double-buffered: the next batch's
-// loads are issued before the current batch is computed, so every wave keeps
-// memory requests in flight while it works. store(j, row, v0, v1) is called
-// once per (token j, row) by one lane.
-constexpr int kBatchRows = 2;
-
-template <int FMT, int BITS, int CPL, bool GATEUP>
+// go in batches of BR per wave, double-buffered: the next batch's loads are
+// issued before the current batch is computed, so every wave keeps memory
+// requests in flight while it works. store(j, row, v0, v1) is called once per
+// (token j, row) by one lane. Small batches keep fewer bytes in flight per
+// wave, which lowers the queueing latency when every wave of the chip streams
+// at once; the callers pick BR per projection.
+template <int FMT, int BITS, int CPL, bool GATEUP, int BR>
 struct RowBatch {
-  RowRegs<FMT, BITS, CPL> r0[kBatchRows];
-  RowRegs<FMT, BITS, CPL> r1[GATEUP ? kBatchRows : 1];
+  RowRegs<FMT, BITS, CPL> r0[BR];
+  RowRegs<FMT, BITS, CPL> r1[GATEUP ? BR : 1];
 };
 
-template <int FMT, int BITS, int CPL, bool GATEUP>
-__device__ __forceinline__ void load_batch(RowBatch<FMT, BITS, CPL, GATEUP>& b, const QMat& q0, const QMat& q1,
-                                           int r0, int r_end, int lane, int nchunks) {
+template <int FMT, int BITS, int CPL, bool GATEUP, int BR>
+__device__ __forceinline__ void load_batch(RowBatch<FMT, BITS, CPL, GATEUP, BR>& b, const QMat& q0,
+                                           const QMat& q1, int r0, int r_end, int lane, int nchunks) {
 #pragma unroll
-  for (int i = 0; i < kBatchRows; ++i) {
+  for (int i = 0; i < BR; ++i) {
     const int r = min(r0 + i, r_end - 1);
     load_row<FMT, BITS, CPL>(b.r0[i], q0, r, lane, nchunks);
     if constexpr (GATEUP) load_row<FMT, BITS, CPL>(b.r1[i], q1, r, lane, nchunks);
   }
 }
 
-template <int FMT, int BITS, int CPL, int NT, bool GATEUP, class Store>
-__device__ __forceinline__ void compute_batch(const RowBatch<FMT, BITS, CPL, GATEUP>& b,
+template <int FMT, int BITS, int CPL, int NT, bool GATEUP, int BR, class Store>
+__device__ __forceinline__ void compute_batch(const RowBatch<FMT, BITS, CPL, GATEUP, BR>& b,
                                               const XRegs<FMT, BITS, CPL, NT>& xr, int r0, int r_end, int lane,
                                               int nchunks, Store& store) {
-  constexpr int N = kBatchRows * NT;
+  constexpr int N = BR * NT;
   float acc0[N], acc1[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) acc0[i] = acc1[i] = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kBatchRows; ++i) {
+  for (int i = 0; i < BR; ++i) {
     row_dot<FMT, BITS, CPL, NT>(b.r0[i], xr, acc0 + i * NT, lane, nchunks);
     if constexpr (GATEUP) row_dot<FMT, BITS, CPL, NT>(b.r1[i], xr, acc1 + i * NT, lane, nchunks);
   }
@@ -328,7 +328,7 @@ __device__ __forceinline__ void compute_batch(const RowBatch<FMT, BITS, CPL, GAT
   if (reduce_multi_writer<N>(lane) && r0 + ri < r_end) store(j, r0 + ri, s0, s1);
 }
 
-template <int FMT, int BITS, int CPL, int NT, bool GATEUP, class Store>
+template <int FMT, int BITS, int CPL, int NT, bool GATEUP, int BR, class Store>
 __device__ __forceinline__ void stream_rows(const QMat& q0, const QMat& q1, const XRaw<CPL, NT>& xw,
                                             const bool (&xvalid)[NT], int r_begin, int r_end, int lane,
                                             int nchunks, Store store) {
@@ -337,19 +337,19 @@ __device__ __forceinline__ void stream_rows(const QMat& q0, const QMat& q1, cons
   // for every load in flight, which would undo the double buffering. The
   // activations (issued by the caller) are unpacked once the first rows are
   // in flight.
-  RowBatch<FMT, BITS, CPL, GATEUP> A, B;
+  RowBatch<FMT, BITS, CPL, GATEUP, BR> A, B;
   int r = r_begin;
-  load_batch<FMT, BITS, CPL, GATEUP>(A, q0, q1, r, r_end, lane, nchunks);
+  load_batch<FMT, BITS, CPL, GATEUP, BR>(A, q0, q1, r, r_end, lane, nchunks);
   XRegs<FMT, BITS, CPL, NT> xr;
   finish_x<FMT, BITS, CPL, NT>(xr, xw, xvalid, lane, nchunks);
   while (true) {
-    load_batch<FMT, BITS, CPL, GATEUP>(B, q0, q1, r + kBatchRows, r_end, lane, nchunks);
-    compute_batch<FMT, BITS, CPL, NT, GATEUP>(A, xr, r, r_end, lane, nchunks, store);
-    if (r + kBatchRows >= r_end) break;
-    load_batch<FMT, BITS, CPL, GATEUP>(A, q0, q1, r + 2 * kBatchRows, r_end, lane, nchunks);
-    compute_batch<FMT, BITS, CPL, NT, GATEUP>(B, xr, r + kBatchRows, r_end, lane, nchunks, store);
-    if (r + 2 * kBatchRows >= r_end) break;
-    r += 2 * kBatchRows;
+    load_batch<FMT, BITS, CPL, GATEUP, BR>(B, q0, q1, r + BR, r_end, lane, nchunks);
+    compute_batch<FMT, BITS, CPL, NT, GATEUP, BR>(A, xr, r, r_end, lane, nchunks, store);
+    if (r + BR >= r_end) break;
+    load_batch<FMT, BITS, CPL, GATEUP, BR>(A, q0, q1, r + 2 * BR, r_end, lane, nchunks);
+    compute_batch<FMT, BITS, CPL, NT, GATEUP, BR>(B, xr, r + BR, r_end, lane, nchunks, store);
+    if (r + 2 * BR >= r_end) break;
+    r += 2 * BR;
   }
 }
 
@@ -435,14 +435,14 @@ __device__ __forceinline__ void ffn_stream_body(const StreamArgs& a, int bid, in
     load_x_raw<CPL, NT>(xw, xrow, lane, nchunks);
 
     if constexpr (GATEUP) {
-      stream_rows<FMT, BITS, CPL, NT, true>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
+      stream_rows<FMT, BITS, CPL, NT, true, 1>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
                                             [&](int j, int r, float g, float u) {
                                               if (p0 + j < p1)
                                                 a.h[static_cast<size_t>(p0 + j) * rows + r] =
                                                     static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * u));
                                             });
     } else {
-      stream_rows<FMT, BITS, CPL, NT, false>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
+      stream_rows<FMT, BITS, CPL, NT, false, 2>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
                                              [&](int j, int r, float y, float) {
                                                if (p0 + j < p1) {
                                                  const int slot = a.shared ? p0 + j : min(max(a.perm[p0 + j], 0), n - 1);

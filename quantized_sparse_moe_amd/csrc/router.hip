@@ -12,13 +12,14 @@
 namespace qsmoe {
 
 // ---------------------------------------------------------------------------
-// Logits, few tokens: one wave per (expert, TT tokens).
+// Logits, few tokens: one workgroup per (expert, TT tokens), split-K over
+// its four waves.
 // ---------------------------------------------------------------------------
 template <int TT>
 __global__ __launch_bounds__(256) void k_logits_gemv(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                                      int T, int E, int d, float* __restrict__ logits) {
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e < E) logits_wave<TT>(x, wr, T, E, d, e, blockIdx.y * TT, logits);
+  __shared__ float s_part[4 * TT];
+  logits_wg<TT>(x, wr, T, E, d, blockIdx.x, blockIdx.y * TT, logits, s_part);
 }
 
 // ---------------------------------------------------------------------------
@@ -257,11 +258,11 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E
     hipLaunchKernelGGL(k_logits_mfma<1>, dim3((E + 63) / 64, (T + 15) / 16), dim3(256), 0, s, x, wr, T, E, d,
                        logits);
   } else if (T == 1) {
-    hipLaunchKernelGGL(k_logits_gemv<1>, dim3((E + 3) / 4, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
+    hipLaunchKernelGGL(k_logits_gemv<1>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else if (T == 2) {
-    hipLaunchKernelGGL(k_logits_gemv<2>, dim3((E + 3) / 4, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
+    hipLaunchKernelGGL(k_logits_gemv<2>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else {
-    hipLaunchKernelGGL(k_logits_gemv<4>, dim3((E + 3) / 4, (T + 3) / 4), dim3(256), 0, s, x, wr, T, E, d, logits);
+    hipLaunchKernelGGL(k_logits_gemv<4>, dim3(E, (T + 3) / 4), dim3(256), 0, s, x, wr, T, E, d, logits);
   }
   return hipGetLastError();
 }

@@ -51,24 +51,30 @@ __device__ __forceinline__ void score_key(float l, const float* __restrict__ bia
   key = pack_key(s + (bias ? bias[e] : 0.0f), e);
 }
 
-// Logits of expert e for tokens t0 .. t0+TT-1 (clamped to T) by one wave:
-// lanes stride the hidden dimension 8 values at a time (32 B of Wr, 16 B of x
-// per token) with up to 4096 columns' loads issued in one batch, then one
-// multi-value wave reduction. The accumulation order per lane is fixed
-// (ascending column), so every caller gets identical logits. With `keys`, the
-// writer lane also stores each token's score and ranking key.
+// Logits of expert e for tokens t0 .. t0+TT-1 (clamped to T) by the four
+// waves of a workgroup: wave w takes the columns [w d/4, (w+1) d/4) (d % 32
+// == 0; the quarter boundaries are multiples of 8), its lanes striding them 8
+// values at a time (32 B of Wr, 16 B of x per token) with every load of the
+// quarter (up to 1024 columns) issued in one batch, then one multi-value wave
+// reduction; wave 0 adds the four partial sums in wave order. The order of
+// every addition is fixed, so every caller gets identical logits. With
+// `keys`, the writer lane also stores each token's score and ranking key.
+// Must be called by all four waves of the workgroup with the same e and t0;
+// s_part holds 4 * TT floats of LDS.
 template <int TT>
-__device__ __forceinline__ void logits_wave(const uint16_t* __restrict__ x, const float* __restrict__ wr, int T,
-                                            int E, int d, int e, int t0, float* __restrict__ logits,
-                                            const float* __restrict__ bias = nullptr, uint64_t* keys = nullptr,
-                                            float* scores = nullptr) {
-  const int lane = lane_id();
+__device__ __forceinline__ void logits_wg(const uint16_t* __restrict__ x, const float* __restrict__ wr, int T, int E,
+                                          int d, int e, int t0, float* __restrict__ logits, float* s_part,
+                                          const float* __restrict__ bias = nullptr, uint64_t* keys = nullptr,
+                                          float* scores = nullptr) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int q8 = d >> 3;  // columns in units of 8
+  const int c_begin = ((q8 * wave) >> 2) << 3, c_end = ((q8 * (wave + 1)) >> 2) << 3;
   float acc[TT];
 #pragma unroll
   for (int j = 0; j < TT; ++j) acc[j] = 0.0f;
   const float* wrow = wr + static_cast<size_t>(e) * d;
-  constexpr int kSteps = 8;  // 8 * 512 columns per batch
-  for (int base0 = lane * 8; base0 < d; base0 += kSteps * 512) {
+  constexpr int kSteps = 2;  // 2 * 512 columns per batch
+  for (int base0 = c_begin + lane * 8; base0 < c_end; base0 += kSteps * 512) {
     float4 w0[kSteps], w1[kSteps];
     uint4 xv[kSteps][TT];
 #pragma unroll
@@ -84,7 +90,7 @@ __device__ __forceinline__ void logits_wave(const uint16_t* __restrict__ x, cons
     }
 #pragma unroll
     for (int q = 0; q < kSteps; ++q) {
-      if (base0 + q * 512 >= d) break;
+      if (base0 + q * 512 >= c_end) break;
 #pragma unroll
       for (int j = 0; j < TT; ++j) {
         float a = acc[j];
@@ -102,10 +108,13 @@ __device__ __forceinline__ void logits_wave(const uint16_t* __restrict__ x, cons
   }
   const float r = wave_reduce_multi<TT>(acc);
   const int j = reduce_multi_index<TT>(lane);
-  if (reduce_multi_writer<TT>(lane) && t0 + j < T) {
+  if (reduce_multi_writer<TT>(lane)) s_part[wave * TT + j] = r;
+  __syncthreads();
+  if (wave == 0 && reduce_multi_writer<TT>(lane) && t0 + j < T) {
+    const float l = ((s_part[j] + s_part[TT + j]) + s_part[2 * TT + j]) + s_part[3 * TT + j];
     const size_t o = static_cast<size_t>(t0 + j) * E + e;
-    logits[o] = r;
-    if (keys != nullptr) score_key(r, bias, e, scores[o], keys[o]);
+    logits[o] = l;
+    if (keys != nullptr) score_key(l, bias, e, scores[o], keys[o]);
   }
 }
 
