@@ -285,6 +285,9 @@ bool decode_path_supported(const DecodeArgs& a) {
 #ifndef QSMOE_DEC_GU_MIN_ROWS
 #define QSMOE_DEC_GU_MIN_ROWS 2
 #endif
+#ifndef QSMOE_DEC_SH_MIN_ROWS
+#define QSMOE_DEC_SH_MIN_ROWS 2
+#endif
 #ifndef QSMOE_DEC_DN_MIN_ROWS
 #define QSMOE_DEC_DN_MIN_ROWS 4
 #endif
@@ -328,7 +331,7 @@ hipError_t launch_dec_router(const DecodeArgs& a0, hipStream_t s) {
   const int scpl = a.has_shared ? dec_cpl(a.sgate.cols) : 1;
   const int snt = dec_shared_nt(a, scpl);
   unsigned grid = a.n_logit_blocks;
-  if (snt > 0) grid += dec_grid(static_cast<int64_t>((a.T + snt - 1) / snt) * a.sgate.rows, 2);
+  if (snt > 0) grid += dec_grid(static_cast<int64_t>((a.T + snt - 1) / snt) * a.sgate.rows, QSMOE_DEC_SH_MIN_ROWS);
   const int tt = a.T <= 1 ? 1 : (a.T <= 2 ? 2 : 4);
 #define QSMOE_K1(CP, NT_)                                                                   \
   do {                                                                                      \

@@ -43,11 +43,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;  // plain 16-byte register quad
 
-constexpr int kMT = 128;                 // tokens per workgroup tile
 constexpr int kKT = 128;                 // inputs per K step
 constexpr int kALdsStride = kKT + 8;     // bf16 elements per LDS row (272 bytes)
-constexpr int kRB = 2;                   // 16-column blocks per wave
-constexpr int kMB = kMT / 16;            // 16-token blocks per wave
 
 struct MfmaArgs {
   QMat m0, m1;             // gate, up (GATEUP) or down
@@ -126,22 +123,25 @@ __device__ bool tile_of_block(const MfmaArgs& a, int n_ntiles, int32_t* s_off, i
   return true;
 }
 
-template <bool GATEUP>
+template <bool GATEUP, int MT, int RB>
 __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
-  constexpr int NTILE = GATEUP ? 64 : 128;    // output rows per workgroup (per matrix)
+  constexpr int HB = GATEUP ? RB / 2 : RB;    // 16-row blocks per matrix per wave
+  constexpr int NTILE = 4 * HB * 16;          // output rows per workgroup (per matrix)
+  constexpr int MB = MT / 16;                 // 16-token blocks per wave
+  constexpr int ACH = MT * 16 / 256;          // 16-byte activation chunks per thread per K step
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ int32_t s_mt[kMaxExperts + 1];
-  __shared__ int32_t s_src[kMT];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kMT][kALdsStride];
+  __shared__ int32_t s_src[MT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int wn = wave;
   const int n = a.T * a.k;
   const int rows = a.m0.rows, cols = a.m0.cols;
   Tile t;
-  if (!tile_of_block<kMT>(a, rows / NTILE, s_off, s_mt, t)) return;
+  if (!tile_of_block<MT>(a, rows / NTILE, s_off, s_mt, t)) return;
   const int e = t.e, p0 = t.p0, count = t.count, ntile = t.ntile;
-  if (tid < kMT) {
+  if (tid < MT) {
     const int p = p0 + min(tid, count - 1);
     s_src[tid] = GATEUP ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
   }
@@ -151,36 +151,36 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   // token row t / 16 + 16 i, so 16 consecutive lanes read one row's 256
   // contiguous bytes of the K step.
   const int a_chunk = tid & 15, a_row0 = tid >> 4;
-  uint32_t a_off[8];  // element offsets of this thread's 8 rows (+ its chunk)
+  uint32_t a_off[ACH];  // element offsets of this thread's rows (+ its chunk)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a_off[i] = static_cast<uint32_t>(s_src[a_row0 + 16 * i]) * cols + a_chunk * 8;
-  auto load_a = [&](u32x4_t (&ar)[8], int k0) {
+  for (int i = 0; i < ACH; ++i) a_off[i] = static_cast<uint32_t>(s_src[a_row0 + 16 * i]) * cols + a_chunk * 8;
+  auto load_a = [&](u32x4_t (&ar)[ACH], int k0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ar[i] = *reinterpret_cast<const u32x4_t*>(a.x + a_off[i] + k0);
+    for (int i = 0; i < ACH; ++i) ar[i] = *reinterpret_cast<const u32x4_t*>(a.x + a_off[i] + k0);
   };
-  auto store_a = [&](const u32x4_t (&ar)[8], int buf) {
+  auto store_a = [&](const u32x4_t (&ar)[ACH], int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row0 + 16 * i][a_chunk * 8]) = ar[i];
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row0 + 16 * i][a_chunk * 8]) = ar[i];
   };
 
-  // B: this wave's 2 column blocks (gate/up: 16 rows of gate + the same 16 of up)
+  // B: this wave's RB column blocks (gate/up: HB blocks of gate + the same rows of up)
   const QMat w0 = expert_slice(a.m0, e);
   const QMat w1 = expert_slice(a.m1, e);
   const int g = lane >> 4, r16 = lane & 15;
-  const int row0 = ntile * NTILE + wn * (GATEUP ? 16 : 32) + r16;  // row of block 0 for this lane
+  const int row0 = ntile * NTILE + wn * HB * 16 + r16;  // row of block 0 for this lane
   const size_t rw = static_cast<size_t>(w0.row_words), rg = static_cast<size_t>(w0.row_groups);
-  // byte addresses of this lane's rows: block rb is row0 + 16 rb (down) or
-  // row0 of gate (rb = 0) / up (rb = 1)
+  // byte addresses of this lane's rows: block rb is row0 + 16 (rb % HB) of
+  // gate or down (rb < HB) / up (rb >= HB)
   const uint8_t* c0 = reinterpret_cast<const uint8_t*>(w0.codes) + (static_cast<size_t>(row0) * rw + 4 * g) * 4;
   const uint8_t* c1 = reinterpret_cast<const uint8_t*>(w1.codes) + (static_cast<size_t>(row0) * rw + 4 * g) * 4;
   const uint8_t* e0p = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(row0) * rg + g;
   const uint8_t* e1p = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(row0) * rg + g;
   const size_t cstep = 16 * rw * 4, estep = 16 * rg;
-  auto load_b = [&](u32x4_t (&bv)[kRB], uint32_t (&sv)[kRB], int k0) {
+  auto load_b = [&](u32x4_t (&bv)[RB], uint32_t (&sv)[RB], int k0) {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      const bool second = GATEUP && rb == 1;
-      const int blk = GATEUP ? 0 : rb;
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool second = GATEUP && rb >= HB;
+      const int blk = rb % HB;
       const uint8_t* cp = (second ? c1 : c0) + blk * cstep + k0 / 2;
       const uint8_t* ep = (second ? e1p : e0p) + blk * estep + k0 / 32;
       bv[rb] = *reinterpret_cast<const u32x4_t*>(cp);
@@ -188,27 +188,27 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
     }
   };
 
-  f32x4_t acc[kMB][kRB];
+  f32x4_t acc[MB][RB];
 #pragma unroll
-  for (int i = 0; i < kMB; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < kRB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // the K loop, specialised on the number of 16-token blocks that hold
   // tokens, so that no MFMA sits behind a branch
-  const int valid_mb = min(kMB, (count + 15) / 16);
+  const int valid_mb = min(MB, (count + 15) / 16);
   const int nsteps = cols / kKT;
   // Software pipeline over K steps: during step ks the activations of step
   // ks + 2 and the weights of step ks + 1 are in flight, the activations of
   // step ks + 1 (already in registers) go to the other LDS buffer at the end.
   // Register sets alternate between even and odd steps (loop unrolled by 2).
-  u32x4_t a_reg0[8], a_reg1[8];
-  u32x4_t b_reg0[kRB], b_reg1[kRB];
-  uint32_t e_reg0[kRB], e_reg1[kRB];
+  u32x4_t a_reg0[ACH], a_reg1[ACH];
+  u32x4_t b_reg0[RB], b_reg1[RB];
+  uint32_t e_reg0[RB], e_reg1[RB];
   auto kloop = [&](auto nmb_tag) {
     constexpr int NMB = decltype(nmb_tag)::value;
-    auto step = [&](int ks, u32x4_t (&a_ld)[8], const u32x4_t (&a_st)[8], const u32x4_t (&b_use)[kRB],
-                    const uint32_t (&e_use)[kRB], u32x4_t (&b_ld)[kRB], uint32_t (&e_ld)[kRB]) {
+    auto step = [&](int ks, u32x4_t (&a_ld)[ACH], const u32x4_t (&a_st)[ACH], const u32x4_t (&b_use)[RB],
+                    const uint32_t (&e_use)[RB], u32x4_t (&b_ld)[RB], uint32_t (&e_ld)[RB]) {
       const int buf = ks & 1;
       load_a(a_ld, min(ks + 2, nsteps - 1) * kKT);
       load_b(b_ld, e_ld, min(ks + 1, nsteps - 1) * kKT);
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
         for (int mb = 0; mb < NMB; ++mb)
           af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][mb * 16 + r16][32 * g + 8 * s]);
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
+        for (int rb = 0; rb < RB; ++rb) {
           if constexpr (NMB > 0) {
             const bf16x8_t bf = fp4_to_bf16x8(b_use[rb][s], e8m0_to_f32(e_use[rb]));
 #pragma unroll
@@ -243,33 +243,44 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
     }
     if (ks < nsteps) step(ks, a_reg1, a_reg0, b_reg0, e_reg0, b_reg1, e_reg1);
   };
-  switch (valid_mb) {
-    case 8: kloop(std::integral_constant<int, 8>{}); break;
-    case 7: kloop(std::integral_constant<int, 7>{}); break;
-    case 6: kloop(std::integral_constant<int, 6>{}); break;
-    case 5: kloop(std::integral_constant<int, 5>{}); break;
-    case 4: kloop(std::integral_constant<int, 4>{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}); break;
-    default: kloop(std::integral_constant<int, 1>{}); break;
+  if constexpr (MB == 8) {
+    switch (valid_mb) {
+      case 8: kloop(std::integral_constant<int, 8>{}); break;
+      case 7: kloop(std::integral_constant<int, 7>{}); break;
+      case 6: kloop(std::integral_constant<int, 6>{}); break;
+      case 5: kloop(std::integral_constant<int, 5>{}); break;
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      default: kloop(std::integral_constant<int, 1>{}); break;
+    }
+  } else {
+    switch (valid_mb) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      default: kloop(std::integral_constant<int, 1>{}); break;
+    }
   }
 
   // epilogue: lane holds rows 4 * g + i (tokens) of column r16 (output row)
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     if (mb >= valid_mb) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int tl = mb * 16 + 4 * g + i;
       if (tl >= count) continue;
       if constexpr (GATEUP) {
-        a.h[static_cast<size_t>(p0 + tl) * rows + row0] =
-            static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][0][i]) * acc[mb][1][i]));
+        uint16_t* hrow = a.h + static_cast<size_t>(p0 + tl) * rows + row0;
+#pragma unroll
+        for (int rb = 0; rb < HB; ++rb)
+          hrow[rb * 16] = static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][rb][i]) * acc[mb][rb + HB][i]));
       } else {
         const int slot = min(max(a.perm[p0 + tl], 0), n - 1);
         float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
 #pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) yrow[rb * 16] = acc[mb][rb][i];
+        for (int rb = 0; rb < RB; ++rb) yrow[rb * 16] = acc[mb][rb][i];
       }
     }
   }
@@ -591,9 +602,18 @@ template <bool GATEUP>
 static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   const QMat& m = a.m0;
   if (m.fmt == 1) {
-    constexpr int NTILE = GATEUP ? 64 : 128;
-    hipLaunchKernelGGL((k_mfma_mxfp4<GATEUP>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, kMT)), dim3(256), 0, s,
-                       a);
+    // measured: gate/up best with 128-token tiles x 32 columns per wave, down
+    // with 64-token tiles x 64 columns per wave
+    constexpr int MT = GATEUP ? 128 : 64, RB = GATEUP ? 2 : 4;
+    constexpr int NTILE = 4 * (GATEUP ? RB / 2 : RB) * 16;
+    if (m.rows % NTILE == 0) {
+      hipLaunchKernelGGL((k_mfma_mxfp4<GATEUP, MT, RB>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, MT)),
+                         dim3(256), 0, s, a);
+    } else {
+      constexpr int NT2 = GATEUP ? 64 : 128;
+      hipLaunchKernelGGL((k_mfma_mxfp4<GATEUP, 128, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NT2, 128)),
+                         dim3(256), 0, s, a);
+    }
   } else if (static_cast<int64_t>(a.T) * a.k < 16LL * a.E || m.group == 32) {
     launch_affine<GATEUP, 16>(a, s);  // buckets average under 16 tokens (or 4 groups per step)
   } else {
