@@ -42,12 +42,16 @@ bool gemv_supported(const QMat& m) {
   return m.fmt == 1 && m.bits == 4 && m.group == 32;
 }
 
-// Tokens handled per pass over the rows, from the mean bucket size.
+// Tokens handled per pass over the rows, from the mean bucket size (the
+// activations of NT tokens x CPL chunks are held in registers).
+#ifndef QSMOE_GEMV_MAX_NTC
+#define QSMOE_GEMV_MAX_NTC 8
+#endif
 static int tokens_per_pass(int T, int k, int E, int cpl, int shared) {
   const int buckets = shared ? 1 : (T * k < E ? T * k : E);
   const int per = shared ? T : (T * k + buckets - 1) / buckets;
   int nt = per <= 1 ? 1 : (per <= 2 ? 2 : 4);
-  while (nt * cpl > 4) nt >>= 1;
+  while (nt * cpl > QSMOE_GEMV_MAX_NTC) nt >>= 1;
   return nt;
 }
 
@@ -82,8 +86,11 @@ static int tokens_per_pass(int T, int k, int E, int cpl, int shared) {
   } else if ((CPL_) == 2 && (NT_) == 1) {                    \
     constexpr int CP = 2, NTK = 1;                           \
     __VA_ARGS__                                              \
-  } else if ((CPL_) == 2) {                                  \
+  } else if ((CPL_) == 2 && (NT_) == 2) {                   \
     constexpr int CP = 2, NTK = 2;                           \
+    __VA_ARGS__                                              \
+  } else if ((CPL_) == 2) {                                  \
+    constexpr int CP = 2, NTK = 4;                           \
     __VA_ARGS__                                              \
   } else {                                                   \
     constexpr int CP = 4, NTK = 1;                           \
