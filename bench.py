@@ -11,9 +11,10 @@ torch.cuda.synchronize() on each side; inputs and weights are resident in HBM.
 Steps rotate over several device copies of the layer so that no step finds its
 weights in the 256 MB Infinity Cache left there by a recent step.
 
-Also reported: the dominant kernel's roofline from HIP events recorded on the
-library's stream between kernels (moe_forward_probed), and the CPU oracle timed
-on a bounded sample of the same workload on the host cores.
+Also reported: the dominant kernel's roofline from HIP events that the
+dispatches on the library's stream timestamp at kernel start and end
+(moe_forward_probed), and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
 """
 from __future__ import annotations
 
@@ -262,8 +263,9 @@ def main():
     ms = start.elapsed_time(stop) / K
     assert qm.device_error(ws) == 0
 
-    # per-kernel durations: events between kernels, host kept ahead of the GPU
-    n_ev = 17
+    # per-kernel durations: each kernel's own start/stop timestamps (events
+    # taken by the dispatch), on the library's stream
+    n_ev = 32
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     for e in evs:
         e.record()  # torch creates the HIP event on first use
@@ -271,11 +273,10 @@ def main():
     probe_steps = min(K, 64)
     sums = {}
     for i in range(probe_steps):
-        torch.cuda._sleep(2_000_000)  # lets the host enqueue the step before it runs
         names = qm.forward_probed(layers[i % copies], xs[i % n_x], toks[i % n_x], out, ws, evs)
         torch.cuda.synchronize()
         for j, n in enumerate(names):
-            sums.setdefault(n, []).append(evs[j].elapsed_time(evs[j + 1]) * 1e3)
+            sums.setdefault(n, []).append(evs[2 * j].elapsed_time(evs[2 * j + 1]) * 1e3)
     kern = {n: float(np.mean(v)) for n, v in sums.items()}
     dom = max(kern, key=kern.get)
     dom_bytes = kernel_bytes(dom, cfg, base, T, touched_mean)

@@ -209,11 +209,14 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
 moe_status moe_router_logits(const moe_router* router, const uint16_t* x_bf16, int32_t T,
                              float* logits, hipStream_t stream);
 
-/* moe_forward with timing probes: records events[0] on `stream` before the
- * first kernel and events[i] after the i-th kernel, and stores the kernels'
- * names (static strings) in names[i-1] and their count in *n_kernels.
- * n_events must exceed the number of kernels (at most 16 are launched). The
- * caller creates the events. Same results as moe_forward. */
+/* moe_forward with timing probes: kernel i is launched with the event pair
+ * events[2i] (start) and events[2i+1] (stop), which the dispatch itself
+ * timestamps when the kernel begins and ends, so their elapsed time is the
+ * kernel's execution time alone. Its name (a static string) goes to names[i]
+ * and the number of kernels to *n_kernels. n_events must be at least twice
+ * the number of kernels (at most 16 are launched, so 32 always suffice);
+ * otherwise MOE_ERR_INVALID_ARG after the step has run. The caller creates
+ * the events (timing enabled). Same results as moe_forward. */
 moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids,
                               int32_t T, int32_t out_dtype, void* out, void* ws, size_t ws_bytes,
                               hipStream_t stream, hipEvent_t* events, int32_t n_events, const char** names,

@@ -221,8 +221,10 @@ def forward(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tenso
 
 def forward_probed(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tensor], out: torch.Tensor,
                    ws: torch.Tensor, events, stream=None):
-    """moe_forward with an event recorded before the first and after every
-    kernel; returns the kernels' names. ``events`` are torch.cuda.Event(enable_timing=True)."""
+    """moe_forward with a (start, stop) event pair per kernel, timestamped by
+    the dispatch itself: kernel i runs between events[2i] and events[2i+1].
+    Returns the kernels' names. ``events`` are torch.cuda.Event(enable_timing=True),
+    already created on the device (record them once first)."""
     x = _bits_tensor(x)
     n = len(events)
     evs = (ctypes.c_void_p * n)(*[ctypes.c_void_p(e.cuda_event) for e in events])

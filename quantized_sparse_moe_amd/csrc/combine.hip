@@ -48,9 +48,9 @@ hipError_t launch_combine(const float* y_slot, const float* w, const float* y_sh
                           int out_f32, void* out, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((d / 4 + 255) / 256) * T), block(256);
   if (out_f32)
-    hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, y_slot, w, y_shared, T, k, d, out);
+    QSMOE_LAUNCH(k_combine<1>, grid, block, 0, s, y_slot, w, y_shared, T, k, d, out);
   else
-    hipLaunchKernelGGL(k_combine<0>, grid, block, 0, s, y_slot, w, y_shared, T, k, d, out);
+    QSMOE_LAUNCH(k_combine<0>, grid, block, 0, s, y_slot, w, y_shared, T, k, d, out);
   return hipGetLastError();
 }
 
@@ -60,7 +60,7 @@ __global__ void k_fill_i32(int32_t* p, int32_t v, int n) {
 }
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, v, n);
+  QSMOE_LAUNCH(k_fill_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
 

@@ -336,11 +336,11 @@ hipError_t launch_dec_router(const DecodeArgs& a0, hipStream_t s) {
 #define QSMOE_K1(CP, NT_)                                                                   \
   do {                                                                                      \
     if (tt == 1)                                                                            \
-      hipLaunchKernelGGL((k_dec_router<1, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
+      QSMOE_LAUNCH((k_dec_router<1, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
     else if (tt == 2)                                                                       \
-      hipLaunchKernelGGL((k_dec_router<2, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
+      QSMOE_LAUNCH((k_dec_router<2, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
     else                                                                                    \
-      hipLaunchKernelGGL((k_dec_router<4, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
+      QSMOE_LAUNCH((k_dec_router<4, CP, NT_>), dim3(grid), dim3(256), 0, s, a);       \
   } while (0)
   if (snt == 0) QSMOE_K1(1, 0);
   else if (scpl == 1 && snt == 1) QSMOE_K1(1, 1);
@@ -358,11 +358,11 @@ hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.k * a.gate.rows, QSMOE_DEC_GU_MIN_ROWS)), block(256);
   QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
     if (cpl == 1)
-      hipLaunchKernelGGL((k_dec_gateup<F, B, 1>), grid, block, 0, s, a);
+      QSMOE_LAUNCH((k_dec_gateup<F, B, 1>), grid, block, 0, s, a);
     else if (cpl == 2)
-      hipLaunchKernelGGL((k_dec_gateup<F, B, 2>), grid, block, 0, s, a);
+      QSMOE_LAUNCH((k_dec_gateup<F, B, 2>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((k_dec_gateup<F, B, 4>), grid, block, 0, s, a);
+      QSMOE_LAUNCH((k_dec_gateup<F, B, 4>), grid, block, 0, s, a);
   })
   return hipGetLastError();
 }
@@ -374,9 +374,9 @@ hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s) {
 #define QSMOE_K3(K_)                                                                                   \
   do {                                                                                                 \
     if (a.has_shared)                                                                                  \
-      hipLaunchKernelGGL((k_dec_down_combine<F, B, K_, true>), grid, block, lds, s, a);                \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, true>), grid, block, lds, s, a);                \
     else                                                                                               \
-      hipLaunchKernelGGL((k_dec_down_combine<F, B, K_, false>), grid, block, lds, s, a);               \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, false>), grid, block, lds, s, a);               \
   } while (0)
   QSMOE_DEC_FMT(a.down.fmt, a.down.bits, {
     if (K == 2) QSMOE_K3(2);

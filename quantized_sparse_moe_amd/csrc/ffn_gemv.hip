@@ -113,7 +113,7 @@ hipError_t launch_gateup(const GateUpArgs& g, hipStream_t s) {
   StreamArgs a{g.gate, g.up, g.x, g.T, g.k, g.E, g.offsets, g.perm, g.shared, g.h, nullptr};
   const dim3 grid(stream_grid(g.T, g.k, g.E, nt, g.gate.rows, g.shared)), block(256);
   QSMOE_FMT_SWITCH(g.gate.fmt, g.gate.bits, QSMOE_SHAPE_SWITCH(cpl, nt, {
-    hipLaunchKernelGGL((k_ffn_stream<F, B, CP, NTK, true>), grid, block, 0, s, a);
+    QSMOE_LAUNCH((k_ffn_stream<F, B, CP, NTK, true>), grid, block, 0, s, a);
   }))
   return hipGetLastError();
 }
@@ -124,7 +124,7 @@ hipError_t launch_down(const DownArgs& d, hipStream_t s) {
   StreamArgs a{d.down, d.down, d.h, d.T, d.k, d.E, d.offsets, d.perm, d.shared, nullptr, d.y};
   const dim3 grid(stream_grid(d.T, d.k, d.E, nt, d.down.rows, d.shared)), block(256);
   QSMOE_FMT_SWITCH(d.down.fmt, d.down.bits, QSMOE_SHAPE_SWITCH(cpl, nt, {
-    hipLaunchKernelGGL((k_ffn_stream<F, B, CP, NTK, false>), grid, block, 0, s, a);
+    QSMOE_LAUNCH((k_ffn_stream<F, B, CP, NTK, false>), grid, block, 0, s, a);
   }))
   return hipGetLastError();
 }

@@ -588,14 +588,14 @@ static void launch_affine(const MfmaArgs& a, hipStream_t s) {
   const dim3 grid(mfma_grid(a.T, a.k, a.E, a.m0.rows, NTILE, MT));
   if constexpr (MT == 16) {
     if (a.m0.group == 32) {
-      hipLaunchKernelGGL((k_mfma_affine4<GATEUP, 32, 16>), grid, dim3(256), 0, s, a);
+      QSMOE_LAUNCH((k_mfma_affine4<GATEUP, 32, 16>), grid, dim3(256), 0, s, a);
       return;
     }
   }
   if (a.m0.group == 64)
-    hipLaunchKernelGGL((k_mfma_affine4<GATEUP, 64, MT>), grid, dim3(256), 0, s, a);
+    QSMOE_LAUNCH((k_mfma_affine4<GATEUP, 64, MT>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_mfma_affine4<GATEUP, 128, MT>), grid, dim3(256), 0, s, a);
+    QSMOE_LAUNCH((k_mfma_affine4<GATEUP, 128, MT>), grid, dim3(256), 0, s, a);
 }
 
 template <bool GATEUP>
@@ -607,11 +607,11 @@ static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
     constexpr int MT = GATEUP ? 128 : 64, RB = GATEUP ? 2 : 4;
     constexpr int NTILE = 4 * (GATEUP ? RB / 2 : RB) * 16;
     if (m.rows % NTILE == 0) {
-      hipLaunchKernelGGL((k_mfma_mxfp4<GATEUP, MT, RB>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, MT)),
+      QSMOE_LAUNCH((k_mfma_mxfp4<GATEUP, MT, RB>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, MT)),
                          dim3(256), 0, s, a);
     } else {
       constexpr int NT2 = GATEUP ? 64 : 128;
-      hipLaunchKernelGGL((k_mfma_mxfp4<GATEUP, 128, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NT2, 128)),
+      QSMOE_LAUNCH((k_mfma_mxfp4<GATEUP, 128, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NT2, 128)),
                          dim3(256), 0, s, a);
     }
   } else if (static_cast<int64_t>(a.T) * a.k < 16LL * a.E || m.group == 32) {

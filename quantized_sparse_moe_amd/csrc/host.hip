@@ -145,26 +145,43 @@ FwdLayout forward_layout(const moe_layer& L, int T) {
   return f;
 }
 
-// Optional timing probe of moe_forward_probed: an event after every launch.
+// Optional timing probe of moe_forward_probed: every launch takes the next
+// (start, stop) event pair, timestamped by the dispatch itself, and the
+// name given to mark() labels the launches made since the previous mark().
 struct Probe {
   hipEvent_t* events;
   int32_t n_events;
   const char** names;
-  int32_t count;
+  int32_t count;   // launches that took an event pair
+  int32_t named;   // launches already labelled
   bool overflow;
 };
 thread_local Probe* g_probe = nullptr;
 
-hipError_t mark(hipError_t launched, const char* name, hipStream_t s) {
-  if (launched != hipSuccess || g_probe == nullptr) return launched;
+}  // namespace
+
+namespace qsmoe {
+bool probe_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_probe == nullptr) return false;
   Probe& p = *g_probe;
-  if (p.count + 1 >= p.n_events) {
+  if (2 * (p.count + 1) > p.n_events) {
     p.overflow = true;
-    return launched;
+    return false;
   }
-  p.names[p.count] = name;
+  *start = p.events[2 * p.count];
+  *stop = p.events[2 * p.count + 1];
   p.count += 1;
-  return hipEventRecord(p.events[p.count], s);
+  return true;
+}
+}  // namespace qsmoe
+
+namespace {
+
+hipError_t mark(hipError_t launched, const char* name, hipStream_t) {
+  if (g_probe == nullptr) return launched;
+  Probe& p = *g_probe;
+  for (; p.named < p.count; ++p.named) p.names[p.named] = name;
+  return launched;
 }
 
 template <typename P>
@@ -390,9 +407,8 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
                               int32_t out_dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t* events, int32_t n_events, const char** names, int32_t* n_kernels) {
   if (events == nullptr || names == nullptr || n_kernels == nullptr || n_events < 2) return MOE_ERR_INVALID_ARG;
-  Probe p{events, n_events, names, 0, false};
+  Probe p{events, n_events, names, 0, 0, false};
   *n_kernels = 0;
-  if (T > 0 && hipEventRecord(events[0], stream) != hipSuccess) return MOE_ERR_HIP;
   g_probe = &p;
   const moe_status s = moe_forward(layer, x_bf16, token_ids, T, out_dtype, out, ws, ws_bytes, stream);
   g_probe = nullptr;

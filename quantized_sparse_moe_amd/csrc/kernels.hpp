@@ -2,10 +2,26 @@
 // translation units. Everything here is already validated by the caller.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace qsmoe {
+
+// Kernel launch used by every launcher. When moe_forward_probed is active on
+// this thread, the launch takes the next pair of timing events, which the
+// dispatch itself timestamps at kernel start and end (no launch gap inside).
+bool probe_events(hipEvent_t* start, hipEvent_t* stop);
+
+#define QSMOE_LAUNCH(KERNEL, GRID, BLOCK, LDS, STREAM, ...)                                    \
+  do {                                                                                         \
+    hipEvent_t qsmoe_ev0_, qsmoe_ev1_;                                                         \
+    if (::qsmoe::probe_events(&qsmoe_ev0_, &qsmoe_ev1_))                                       \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, qsmoe_ev0_, qsmoe_ev1_, 0,       \
+                            __VA_ARGS__);                                                      \
+    else                                                                                       \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, STREAM, __VA_ARGS__);                       \
+  } while (0)
 
 // One stacked quantised projection as the kernels see it.
 struct QMat {

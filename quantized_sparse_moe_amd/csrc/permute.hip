@@ -139,7 +139,7 @@ hipError_t launch_permute(const int32_t* ids, int n, int E, int32_t* offsets, in
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_permute),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(kPermWaves * 64), lds, s, ids, n, E, nbits, offsets, perm, err);
+  QSMOE_LAUNCH(k_permute, dim3(1), dim3(kPermWaves * 64), lds, s, ids, n, E, nbits, offsets, perm, err);
   return hipGetLastError();
 }
 

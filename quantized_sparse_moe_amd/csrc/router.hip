@@ -252,17 +252,17 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E, int d, float* logits,
                                 hipStream_t s) {
   if (T > 256) {
-    hipLaunchKernelGGL(k_logits_mfma<4>, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, wr, T, E, d,
+    QSMOE_LAUNCH(k_logits_mfma<4>, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, wr, T, E, d,
                        logits);
   } else if (T > 16) {
-    hipLaunchKernelGGL(k_logits_mfma<1>, dim3((E + 63) / 64, (T + 15) / 16), dim3(256), 0, s, x, wr, T, E, d,
+    QSMOE_LAUNCH(k_logits_mfma<1>, dim3((E + 63) / 64, (T + 15) / 16), dim3(256), 0, s, x, wr, T, E, d,
                        logits);
   } else if (T == 1) {
-    hipLaunchKernelGGL(k_logits_gemv<1>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
+    QSMOE_LAUNCH(k_logits_gemv<1>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else if (T == 2) {
-    hipLaunchKernelGGL(k_logits_gemv<2>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
+    QSMOE_LAUNCH(k_logits_gemv<2>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else {
-    hipLaunchKernelGGL(k_logits_gemv<4>, dim3(E, (T + 3) / 4), dim3(256), 0, s, x, wr, T, E, d, logits);
+    QSMOE_LAUNCH(k_logits_gemv<4>, dim3(E, (T + 3) / 4), dim3(256), 0, s, x, wr, T, E, d, logits);
   }
   return hipGetLastError();
 }
@@ -270,14 +270,14 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E
 hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k, float routed_scale,
                               int32_t* ids, float* w, hipStream_t s) {
   const size_t lds = static_cast<size_t>(4) * E * (sizeof(uint64_t) + sizeof(float));
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), lds, s, logits, bias, T, E, k, routed_scale, ids, w);
+  QSMOE_LAUNCH(k_topk, dim3((T + 3) / 4), dim3(256), lds, s, logits, bias, T, E, k, routed_scale, ids, w);
   return hipGetLastError();
 }
 
 hipError_t launch_router_hash(const uint16_t* x, const float* wr, const int32_t* token_ids,
                               const int32_t* tid2eid, int T, int E, int k, int d, int vocab, float routed_scale,
                               int32_t* ids, float* w, int32_t* err, hipStream_t s) {
-  hipLaunchKernelGGL(k_hash, dim3((T + 3) / 4), dim3(256), 0, s, x, wr, token_ids, tid2eid, T, E, k, d, vocab,
+  QSMOE_LAUNCH(k_hash, dim3((T + 3) / 4), dim3(256), 0, s, x, wr, token_ids, tid2eid, T, E, k, d, vocab,
                      routed_scale, ids, w, err);
   return hipGetLastError();
 }

@@ -141,3 +141,29 @@ def test_deterministic_with_poisoned_workspace():
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(b, c)
     assert qm.device_error(ws) == 0
+
+
+def test_forward_probed_matches_forward_and_times_each_kernel():
+    """The probed step gives the same output; every kernel gets its own event
+    pair with a positive duration, and a too-short event list is rejected."""
+    for cfg in (variant("decode", "probe_dec", 211, T=2, d=512, I=256, E=32, I_shared=256),
+                variant("prefill", "probe_pf", 212, T=64, d=512, I=256, E=8, top_k=2, bias_kind="normal")):
+        layer = synth.gen_layer(cfg)
+        dl = qm.DeviceLayer.from_host(layer)
+        x = xdev(synth.gen_x(cfg, 0))
+        ws = dl.workspace(cfg.T)
+        ref = qm.forward(dl, x, ws=ws, out_dtype="f32").clone()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(32)]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+        names = qm.forward_probed(dl, x, None, out, ws, evs)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        assert names and all(isinstance(n, str) and n for n in names)
+        assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0 for i in range(len(names)))
+        if len(names) > 1:
+            with pytest.raises(RuntimeError):
+                qm.forward_probed(dl, x, None, out, ws, evs[:2])
+            torch.cuda.synchronize()
