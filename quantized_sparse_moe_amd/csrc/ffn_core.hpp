@@ -13,6 +13,13 @@ namespace qsmoe {
 template <int FMT, int BITS>
 struct Codec;
 
+// The pair of bf16 values 128.0 (0x4300) as a vector register: with one
+// operand already in a VGPR, "(w >> n) & mask | k" compiles to a single
+// v_and_or_b32 (the mask takes the one scalar operand a VOP3 may read).
+__device__ __forceinline__ uint32_t bf16x2_128() {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(0x43004300, 0xE4, 0xF, 0xF, false));
+}
+
 // Affine 4-bit: word j holds codes 8j..8j+7; pair m = 4j + i is (8j+i, 8j+i+4).
 template <>
 struct Codec<0, 4> {
@@ -20,10 +27,11 @@ struct Codec<0, 4> {
   static constexpr int lo(int m) { return 8 * (m >> 2) + (m & 3); }
   static constexpr int hi(int m) { return lo(m) + 4; }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[4], uint32_t (&p)[16]) {
+    const uint32_t k = bf16x2_128();
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[4 * j + i] = ((w[j] >> (4 * i)) & 0x000f000fu) | 0x43004300u;
+      for (int i = 0; i < 4; ++i) p[4 * j + i] = ((w[j] >> (4 * i)) & 0x000f000fu) | k;
   }
 };
 
@@ -34,10 +42,11 @@ struct Codec<0, 2> {
   static constexpr int lo(int m) { return 16 * (m >> 3) + (m & 7); }
   static constexpr int hi(int m) { return lo(m) + 8; }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[2], uint32_t (&p)[16]) {
+    const uint32_t k = bf16x2_128();
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) p[8 * j + i] = ((w[j] >> (2 * i)) & 0x00030003u) | 0x43004300u;
+      for (int i = 0; i < 8; ++i) p[8 * j + i] = ((w[j] >> (2 * i)) & 0x00030003u) | k;
   }
 };
 
@@ -53,8 +62,9 @@ struct Codec<0, 3> {
     return ((w[word] >> off) | (w[word + 1] << (32 - off))) & 7u;
   }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[3], uint32_t (&p)[16]) {
+    const uint32_t k = bf16x2_128();
 #pragma unroll
-    for (int m = 0; m < 16; ++m) p[m] = code(w, m) | (code(w, m + 16) << 16) | 0x43004300u;
+    for (int m = 0; m < 16; ++m) p[m] = code(w, m) | (code(w, m + 16) << 16) | k;
   }
 };
 

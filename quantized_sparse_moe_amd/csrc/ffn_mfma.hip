@@ -317,8 +317,9 @@ __device__ __forceinline__ u32x4_t interleave_halves(const u32x4_t& v) {
 }
 
 __device__ __forceinline__ bf16x8_t u4_to_bf16x8_offset128(uint32_t w) {
-  const u32x4_t r{(w & 0x000f000fu) | 0x43004300u, ((w >> 4) & 0x000f000fu) | 0x43004300u,
-                  ((w >> 8) & 0x000f000fu) | 0x43004300u, ((w >> 12) & 0x000f000fu) | 0x43004300u};
+  const uint32_t k = bf16x2_128();
+  const u32x4_t r{(w & 0x000f000fu) | k, ((w >> 4) & 0x000f000fu) | k, ((w >> 8) & 0x000f000fu) | k,
+                  ((w >> 12) & 0x000f000fu) | k};
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
