@@ -21,6 +21,7 @@
 // gate/up/down; shared expert of "DeepSeek-V4-Flash-MLX-4bit"); only the
 // order of the fp32 additions in the combine differs.
 #include <algorithm>
+#include <type_traits>
 
 #include "ffn_core.hpp"
 #include "router_core.hpp"
@@ -154,44 +155,31 @@ __device__ __forceinline__ float row_dot_one(const RowRegs<F, B, CPL>& r, const 
   return acc;
 }
 
-constexpr int kDecRows = 1;  // output rows per batch per wave
-
-template <int F, int B, int K, bool SH>
-struct DownBatch {
-  RowRegs<F, B, 1> r[kDecRows][K];
-  RowRegs<0, 8, 1> rs[kDecRows];
+// The k selected experts' down rows of one output row, as loaded by a wave.
+template <int F, int B, int K>
+struct RoutedRows {
+  RowRegs<F, B, 1> r[K];
 };
 
-template <int F, int B, int K, bool SH>
-__device__ __forceinline__ void dec_load_down(DownBatch<F, B, K, SH>& b, const QMat (&qd)[K], const QMat& qs, int r0,
-                                              int r_end, int lane, int nchunks, int nchunks_sh) {
+template <int F, int B, int K>
+__device__ __forceinline__ void dec_load_routed(RoutedRows<F, B, K>& b, const QMat (&qd)[K], int r, int lane,
+                                                int nchunks) {
 #pragma unroll
-  for (int i = 0; i < kDecRows; ++i) {
-    const int r = min(r0 + i, r_end - 1);
-#pragma unroll
-    for (int j = 0; j < K; ++j) load_row<F, B, 1>(b.r[i][j], qd[j], r, lane, nchunks);
-    if constexpr (SH) load_row<0, 8, 1>(b.rs[i], qs, r, lane, nchunks_sh);
-  }
+  for (int j = 0; j < K; ++j) load_row<F, B, 1>(b.r[j], qd[j], r, lane, nchunks);
 }
 
-template <int F, int B, int K, bool SH>
-__device__ __forceinline__ void dec_compute_down(const DownBatch<F, B, K, SH>& b, const XRegs<F, B, 1, K>& hx,
-                                                 const XRegs<0, 8, 1, 1>& hsx, const float (&wj)[K],
-                                                 const DecodeArgs& a, int t, int r0, int r_end, int lane,
-                                                 int nchunks, int nchunks_sh) {
-  float acc[kDecRows];
+// Output row r of token t: the lane's partial of the shared row (ysh) plus the
+// weighted partials of the k routed rows, reduced over the wave and stored.
+template <int F, int B, int K>
+__device__ __forceinline__ void dec_finish_row(const RoutedRows<F, B, K>& b, const XRegs<F, B, 1, K>& hx,
+                                               const float (&wj)[K], float ysh, const DecodeArgs& a, int t, int r,
+                                               bool valid, int lane, int nchunks) {
+  float v[1] = {ysh};
 #pragma unroll
-  for (int i = 0; i < kDecRows; ++i) {
-    float v = 0.0f;
-#pragma unroll
-    for (int j = 0; j < K; ++j) v += wj[j] * row_dot_one<F, B, 1, K>(b.r[i][j], hx, j, lane, nchunks);
-    if constexpr (SH) v += row_dot_one<0, 8, 1, 1>(b.rs[i], hsx, 0, lane, nchunks_sh);
-    acc[i] = v;
-  }
-  const float y = wave_reduce_multi<kDecRows>(acc);
-  const int ri = reduce_multi_index<kDecRows>(lane);
-  if (reduce_multi_writer<kDecRows>(lane) && r0 + ri < r_end) {
-    const size_t o = static_cast<size_t>(t) * a.down.rows + r0 + ri;
+  for (int j = 0; j < K; ++j) v[0] += wj[j] * row_dot_one<F, B, 1, K>(b.r[j], hx, j, lane, nchunks);
+  const float y = wave_reduce_multi<1>(v);
+  if (reduce_multi_writer<1>(lane) && valid) {
+    const size_t o = static_cast<size_t>(t) * a.down.rows + r;
     if (a.out_f32)
       static_cast<float*>(a.out)[o] = y;
     else
@@ -199,9 +187,14 @@ __device__ __forceinline__ void dec_compute_down(const DownBatch<F, B, K, SH>& b
   }
 }
 
+constexpr int kDecSegRows = 4;  // output rows per segment of a wave's range
+
 // Launch 3: per (token, output row) unit, the k selected experts' down rows
 // and the shared expert's down row against their own h vectors, weighted and
-// summed in one reduction; double-buffered like the streaming core.
+// summed in one reduction. A wave's rows go in segments of kDecSegRows: the
+// segment's shared rows are loaded first (for the first segment, before the
+// routing ids are even read, so that stream hides the ids' round trip), then
+// its routed rows, one row ahead of the arithmetic.
 template <int F, int B, int K, bool SH>
 __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
   QSMOE_TL(2, 0);
@@ -216,7 +209,17 @@ __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
     const int t = static_cast<int>(u / rows);
     const int r_begin = static_cast<int>(u - static_cast<int64_t>(t) * rows);
     const int r_end = static_cast<int>(min<int64_t>(rows, r_begin + (u_end - u)));
-    // ids and weights first, then the h rows, then wait for the ids only
+    // shared h and the first segment's shared rows: no routing needed
+    RowRegs<0, 8, 1> rs[kDecSegRows];
+    XRaw<1, 1> hsw;
+    const uint16_t* srow[1] = {a.h_sh + static_cast<size_t>(t) * Ish};
+    const bool sv[1] = {true};
+    if constexpr (SH) {
+      load_x_raw<1, 1>(hsw, srow, lane, nchunks_sh);
+#pragma unroll
+      for (int i = 0; i < kDecSegRows; ++i) load_row<0, 8, 1>(rs[i], a.sdown, min(r_begin + i, r_end - 1), lane, nchunks_sh);
+    }
+    // ids, weights and the routed h rows
     int id_raw[K];
     float wj[K];
     const uint16_t* hrow[K];
@@ -233,31 +236,41 @@ __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
     }
     XRaw<1, K> hw;
     load_x_raw<1, K>(hw, hrow, lane, nchunks);
-    XRaw<1, 1> hsw;
-    const uint16_t* srow[1] = {a.h_sh + static_cast<size_t>(t) * Ish};
-    const bool sv[1] = {true};
-    if constexpr (SH) load_x_raw<1, 1>(hsw, srow, lane, nchunks_sh);
+    XRegs<0, 8, 1, 1> hsx;
+    if constexpr (SH) finish_x<0, 8, 1, 1>(hsx, hsw, sv, lane, nchunks_sh);
     QMat qd[K];
 #pragma unroll
     for (int j = 0; j < K; ++j)
       qd[j] = expert_slice(a.down, min(max(__builtin_amdgcn_readfirstlane(id_raw[j]), 0), a.E - 1));
-    DownBatch<F, B, K, SH> A, Bb;
-    int r = r_begin;
-    dec_load_down<F, B, K, SH>(A, qd, a.sdown, r, r_end, lane, nchunks, nchunks_sh);
     XRegs<F, B, 1, K> hx;
-    finish_x<F, B, 1, K>(hx, hw, hvalid, lane, nchunks);
-    XRegs<0, 8, 1, 1> hsx;
-    if constexpr (SH) finish_x<0, 8, 1, 1>(hsx, hsw, sv, lane, nchunks_sh);
-    QSMOE_TL(2, 1);
-    while (true) {
-      dec_load_down<F, B, K, SH>(Bb, qd, a.sdown, r + kDecRows, r_end, lane, nchunks, nchunks_sh);
-      dec_compute_down<F, B, K, SH>(A, hx, hsx, wj, a, t, r, r_end, lane, nchunks, nchunks_sh);
-      if (r + kDecRows >= r_end) break;
-      dec_load_down<F, B, K, SH>(A, qd, a.sdown, r + 2 * kDecRows, r_end, lane, nchunks, nchunks_sh);
-      dec_compute_down<F, B, K, SH>(Bb, hx, hsx, wj, a, t, r + kDecRows, r_end, lane, nchunks, nchunks_sh);
-      if (r + 2 * kDecRows >= r_end) break;
-      r += 2 * kDecRows;
-    }
+    auto segment = [&](int seg0, auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
+      if constexpr (SH && !FIRST) {
+#pragma unroll
+        for (int i = 0; i < kDecSegRows; ++i)
+          load_row<0, 8, 1>(rs[i], a.sdown, min(seg0 + i, r_end - 1), lane, nchunks_sh);
+      }
+      RoutedRows<F, B, K> A, Bb;
+      dec_load_routed<F, B, K>(A, qd, min(seg0, r_end - 1), lane, nchunks);
+      if constexpr (FIRST) {
+        finish_x<F, B, 1, K>(hx, hw, hvalid, lane, nchunks);
+        QSMOE_TL(2, 1);
+      }
+      float ysh[kDecSegRows];
+#pragma unroll
+      for (int i = 0; i < kDecSegRows; ++i)
+        ysh[i] = SH ? row_dot_one<0, 8, 1, 1>(rs[i], hsx, 0, lane, nchunks_sh) : 0.0f;
+      dec_load_routed<F, B, K>(Bb, qd, min(seg0 + 1, r_end - 1), lane, nchunks);
+      dec_finish_row<F, B, K>(A, hx, wj, ysh[0], a, t, seg0, seg0 < r_end, lane, nchunks);
+      dec_load_routed<F, B, K>(A, qd, min(seg0 + 2, r_end - 1), lane, nchunks);
+      dec_finish_row<F, B, K>(Bb, hx, wj, ysh[1], a, t, seg0 + 1, seg0 + 1 < r_end, lane, nchunks);
+      dec_load_routed<F, B, K>(Bb, qd, min(seg0 + 3, r_end - 1), lane, nchunks);
+      dec_finish_row<F, B, K>(A, hx, wj, ysh[2], a, t, seg0 + 2, seg0 + 2 < r_end, lane, nchunks);
+      dec_finish_row<F, B, K>(Bb, hx, wj, ysh[3], a, t, seg0 + 3, seg0 + 3 < r_end, lane, nchunks);
+    };
+    static_assert(kDecSegRows == 4, "the segment body is unrolled for 4 rows");
+    segment(r_begin, std::true_type{});
+    for (int seg0 = r_begin + kDecSegRows; seg0 < r_end; seg0 += kDecSegRows) segment(seg0, std::false_type{});
     u += r_end - r_begin;
   }
   __syncthreads();
