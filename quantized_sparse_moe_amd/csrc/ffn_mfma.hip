@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 // holds inputs 32 s + 8 g .. + 7; each lane loads 16 contiguous bytes of its
 // row (inputs 32 g .. + 31) and the words are transposed across the lane
 // groups through the wave's own LDS slot. Scales and biases are fetched once
-// per 4 K steps (lane group j holds step j's) and broadcast with a lane
-// shuffle. The 8 codes of one word decode to bf16 in the order
+// per 8 K steps (lane group q holds steps 2q and 2q + 1) and broadcast with a
+// lane shuffle. The 8 codes of one word decode to bf16 in the order
 // (0, 4, 1, 5, 2, 6, 3, 7) with one and-or per pair; the activations are
 // stored to LDS in that same order within each 8-input chunk.
 // ---------------------------------------------------------------------------
@@ -325,12 +325,6 @@ __device__ __forceinline__ bf16x8_t u4_to_bf16x8_offset128(uint32_t w) {
 
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
 
-template <int G>
-struct AffScaleWords {
-  // packed fp16 words per row per K step: scales (and as many for biases)
-  static constexpr int GPS = kKT / G;
-  static constexpr int W = (GPS + 1) / 2;
-};
 
 template <bool GATEUP, int G, int MT>
 __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
@@ -339,7 +333,6 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
   constexpr int NTILE = 4 * HB * 16;                 // rows per matrix per workgroup
   constexpr int PPG = G / 32;                        // MFMA passes per group
   constexpr int GPS = kKT / G;                       // groups per K step
-  constexpr int SW = AffScaleWords<G>::W;            // scale words per row per step
   constexpr int MB = MT / 16;
   constexpr int ACH = (MT * 16 + 255) / 256;         // 16-byte activation chunks per thread per step
   __shared__ int32_t s_off[kMaxExperts + 1];
@@ -403,24 +396,30 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
       bq[rb] = *reinterpret_cast<const u32x4_t*>(cp);
     }
   };
-  // scales/biases of K steps ks0 .. ks0 + 3: lane group j holds step ks0 + j's
+  // Scales and biases of K steps ks0 .. ks0 + 7: lane group q holds steps
+  // ks0 + 2q and ks0 + 2q + 1, so the 4 lane groups of a row read 8 steps'
+  // values (32 contiguous bytes for groups of 64) with one request per row.
+  constexpr int SWS = GPS == 1 ? 1 : GPS / 2;  // 32-bit words per row per step
   struct Scales {
-    uint32_t s[RB][SW], b[RB][SW];
+    uint32_t s[RB][2][SWS], b[RB][2][SWS];
   };
   auto load_scales = [&](Scales& sc, int ks0) {
-    const int kq = min(ks0 + g, nsteps - 1) * GPS;  // first group of this lane's step
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint16_t* sp = (rb >= HB ? s1p : s0p) + (rb % HB) * gstep + kq;
-      const uint16_t* bp = (rb >= HB ? b1p : b0p) + (rb % HB) * gstep + kq;
-      if constexpr (GPS == 1) {
-        sc.s[rb][0] = *sp;
-        sc.b[rb][0] = *bp;
-      } else {
+    for (int h = 0; h < 2; ++h) {
+      const int kq = min(ks0 + 2 * g + h, nsteps - 1) * GPS;  // first group of that step
 #pragma unroll
-        for (int j = 0; j < SW; ++j) {
-          sc.s[rb][j] = reinterpret_cast<const uint32_t*>(sp)[j];
-          sc.b[rb][j] = reinterpret_cast<const uint32_t*>(bp)[j];
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint16_t* sp = (rb >= HB ? s1p : s0p) + (rb % HB) * gstep + kq;
+        const uint16_t* bp = (rb >= HB ? b1p : b0p) + (rb % HB) * gstep + kq;
+        if constexpr (GPS == 1) {
+          sc.s[rb][h][0] = *sp;
+          sc.b[rb][h][0] = *bp;
+        } else {
+#pragma unroll
+          for (int w = 0; w < SWS; ++w) {
+            sc.s[rb][h][w] = reinterpret_cast<const uint32_t*>(sp)[w];
+            sc.b[rb][h][w] = reinterpret_cast<const uint32_t*>(bp)[w];
+          }
         }
       }
     }
@@ -447,7 +446,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
       const int buf = ks & 1;
       load_b(b_ld, min(ks + 1, nsteps - 1) * kKT);
       load_a(a_ld, min(ks + 2, nsteps - 1) * kKT);
-      if constexpr (J == 0) load_scales(sc_nxt, ks + 4);
+      if constexpr (J == 0) load_scales(sc_nxt, ks + 8);
       // transpose the step's code words across the lane groups (own LDS slot)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) *reinterpret_cast<u32x4_t*>(&s_bt[wave][rb][g][r16][0]) = b_use[rb];
@@ -459,14 +458,14 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int s = 0; s < 4; ++s) qw[rb][s] = s_bt[wave][rb][s][r16][g];
-      // this step's scales and biases live in lane group J
-      uint32_t sw[RB][SW], bw[RB][SW];
+      // this step's scales and biases live in lane group J / 2, half J % 2
+      uint32_t sw[RB][SWS], bw[RB][SWS];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int w = 0; w < SW; ++w) {
-          sw[rb][w] = __shfl(sc_cur.s[rb][w], J * 16 + r16);
-          bw[rb][w] = __shfl(sc_cur.b[rb][w], J * 16 + r16);
+        for (int w = 0; w < SWS; ++w) {
+          sw[rb][w] = __shfl(sc_cur.s[rb][J & 1][w], (J >> 1) * 16 + r16);
+          bw[rb][w] = __shfl(sc_cur.b[rb][J & 1][w], (J >> 1) * 16 + r16);
         }
 
       f32x4_t dg[GPS][NMB][RB], xg[GPS][NMB];
@@ -506,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
               acc[mb][rb][i] = fmaf(sc, dg[j][mb][rb][i], fmaf(bc, xg[j][mb][i], acc[mb][rb][i]));
         }
       }
-      if constexpr (J == 3) sc_cur = sc_nxt;
+      if constexpr (J == 7) sc_cur = sc_nxt;
       store_a(a_st, buf ^ 1);  // after the last step: unused, harmless
       lds_barrier();
     };
@@ -514,6 +513,10 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
     using J1 = std::integral_constant<int, 1>;
     using J2 = std::integral_constant<int, 2>;
     using J3 = std::integral_constant<int, 3>;
+    using J4 = std::integral_constant<int, 4>;
+    using J5 = std::integral_constant<int, 5>;
+    using J6 = std::integral_constant<int, 6>;
+    using J7 = std::integral_constant<int, 7>;
     load_scales(sc_cur, 0);
     load_b(b_reg0, 0);
     load_a(a_reg0, 0);
@@ -521,15 +524,23 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
     load_a(a_reg0, min(1, nsteps - 1) * kKT);
     lds_barrier();
     int ks = 0;
-    for (; ks + 4 <= nsteps; ks += 4) {
+    for (; ks + 8 <= nsteps; ks += 8) {
       step(ks, J0{}, a_reg1, a_reg0, b_reg0, b_reg1);
       step(ks + 1, J1{}, a_reg0, a_reg1, b_reg1, b_reg0);
       step(ks + 2, J2{}, a_reg1, a_reg0, b_reg0, b_reg1);
       step(ks + 3, J3{}, a_reg0, a_reg1, b_reg1, b_reg0);
+      step(ks + 4, J4{}, a_reg1, a_reg0, b_reg0, b_reg1);
+      step(ks + 5, J5{}, a_reg0, a_reg1, b_reg1, b_reg0);
+      step(ks + 6, J6{}, a_reg1, a_reg0, b_reg0, b_reg1);
+      step(ks + 7, J7{}, a_reg0, a_reg1, b_reg1, b_reg0);
     }
     if (ks < nsteps) step(ks, J0{}, a_reg1, a_reg0, b_reg0, b_reg1);
     if (ks + 1 < nsteps) step(ks + 1, J1{}, a_reg0, a_reg1, b_reg1, b_reg0);
     if (ks + 2 < nsteps) step(ks + 2, J2{}, a_reg1, a_reg0, b_reg0, b_reg1);
+    if (ks + 3 < nsteps) step(ks + 3, J3{}, a_reg0, a_reg1, b_reg1, b_reg0);
+    if (ks + 4 < nsteps) step(ks + 4, J4{}, a_reg1, a_reg0, b_reg0, b_reg1);
+    if (ks + 5 < nsteps) step(ks + 5, J5{}, a_reg0, a_reg1, b_reg1, b_reg0);
+    if (ks + 6 < nsteps) step(ks + 6, J6{}, a_reg1, a_reg0, b_reg0, b_reg1);
   };
   if constexpr (MB == 2) {
     if (valid_mb == 2)
