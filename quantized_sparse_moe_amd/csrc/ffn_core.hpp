@@ -176,6 +176,15 @@ __device__ __forceinline__ void load_x(XRegs<FMT, BITS, CPL, NT>& xr, const uint
   finish_x<FMT, BITS, CPL, NT>(xr, xw, xvalid, lane, nchunks);
 }
 
+// 4-bit weight codes are read exactly once per launch: load them
+// non-temporally (measured: 2 % faster decode, no effect on the other
+// streaming launches; slower for the 8-bit shared rows, which keep plain loads).
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_stream_t;
+__device__ __forceinline__ uint4 load_stream16(const uint32_t* p) {
+  const u32x4_stream_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_stream_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // One quantised row as loaded by one lane: raw code words and raw scale /
 // bias bits, converted only when the row is consumed.
 template <int FMT, int BITS, int CPL>
@@ -194,7 +203,7 @@ __device__ __forceinline__ void load_row(RowRegs<FMT, BITS, CPL>& r, const QMat&
     const int c = min(lane + 64 * m, nchunks - 1);
     const uint32_t* src = codes + c * BITS;
     if constexpr (BITS == 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src);
+      const uint4 v = load_stream16(src);
       r.w[m][0] = v.x;
       r.w[m][1] = v.y;
       r.w[m][2] = v.z;
