@@ -210,9 +210,13 @@ def forward(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tenso
     T = x.shape[0]
     if ws is None:
         ws = layer.workspace(T)
-    f32 = out_dtype == "f32"
     if out is None:
+        f32 = out_dtype == "f32"
         out = torch.empty((T, layer.d), dtype=torch.float32 if f32 else torch.bfloat16, device=x.device)
+    else:  # a given output buffer decides the output type
+        if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (T, layer.d):
+            raise ValueError(f"out must be float32 or bfloat16 of shape ({T}, {layer.d})")
+        f32 = out.dtype == torch.float32
     check(_lib.load().moe_forward(ctypes.byref(layer.c), _ptr(x), _ptr(token_ids), T,
                                   _lib.MOE_OUT_F32 if f32 else _lib.MOE_OUT_BF16, _ptr(out), _ptr(ws), ws.numel(),
                                   _stream(stream)), "moe_forward")
