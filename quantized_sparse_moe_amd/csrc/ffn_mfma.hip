@@ -287,7 +287,8 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Affine 4-bit experts (w = s q + b per group of G inputs, fp16 s and b).
+// Affine b-bit experts, b in {2, 3, 4} (w = s q + b per group of G inputs,
+// fp16 s and b).
 //
 // Codes become exact bf16 without a multiply: the bits 0x4300 | q are the
 // value 128 + q. Each MFMA pass covers 32 consecutive inputs, so all of them
@@ -301,14 +302,21 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 // This layout serves buckets of a few tokens (hash routing, mid-size
 // batches), where the weight stream is the cost. Tiles: MT (16 or 32)
 // bucketed tokens x RB * 16 columns per wave (gate/up: RB/2 blocks of gate
-// and the same rows of up), 4 waves per workgroup. Lane group g of pass s
-// holds inputs 32 s + 8 g .. + 7; each lane loads 16 contiguous bytes of its
-// row (inputs 32 g .. + 31) and the words are transposed across the lane
-// groups through the wave's own LDS slot. Scales and biases are fetched once
-// per 8 K steps (lane group q holds steps 2q and 2q + 1) and broadcast with a
-// lane shuffle. The 8 codes of one word decode to bf16 in the order
-// (0, 4, 1, 5, 2, 6, 3, 7) with one and-or per pair; the activations are
-// stored to LDS in that same order within each 8-input chunk.
+// and the same rows of up), 4 waves per workgroup. Each wave streams its 64
+// weight rows in macro steps of ROWB bytes per row (128 bytes: 2 K steps of
+// 4-bit codes, 4 of 2-bit; 192 bytes, 4 K steps, for 3-bit): every load
+// instruction covers whole rows of the macro step (8 rows x 128 bytes, or
+// 4 x 192), so it touches each cache line once; reading 16 rows x 32 bytes
+// per instruction instead measured 25 % less bandwidth from the same
+// number of bytes. The macro step is staged in registers one macro step
+// ahead and written to the wave's own padded LDS slot, from which lane
+// group g of pass s reads the 8-code chunk of inputs 32 s + 8 g .. + 7 and
+// recasts it as one word (code i at bit b i, code i + 4 at bit 16 + b i).
+// Scales and biases are fetched once per 4 K steps (lane group q holds step
+// q) and broadcast with a lane shuffle. A chunk's 8 codes decode
+// to bf16 in the order (0, 4, 1, 5, 2, 6, 3, 7) with one shift and one and-or
+// per pair; the activations are stored to LDS in that same order within each
+// 8-input chunk.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4_t interleave_halves(const u32x4_t& v) {
   // (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
@@ -316,18 +324,21 @@ __device__ __forceinline__ u32x4_t interleave_halves(const u32x4_t& v) {
                  (v[1] & 0xffffu) | (v[3] << 16), (v[1] >> 16) | (v[3] & 0xffff0000u)};
 }
 
-__device__ __forceinline__ bf16x8_t u4_to_bf16x8_offset128(uint32_t w) {
+// The chunk word f (code i at bit BITS i, code i + 4 at bit 16 + BITS i) as
+// the bf16 pairs (128 + q_i, 128 + q_{i+4}), i = 0..3.
+template <int BITS>
+__device__ __forceinline__ bf16x8_t chunk_to_bf16x8_offset128(uint32_t f) {
+  constexpr uint32_t m = ((1u << BITS) - 1u) * 0x10001u;
   const uint32_t k = bf16x2_128();
-  const u32x4_t r{(w & 0x000f000fu) | k, ((w >> 4) & 0x000f000fu) | k, ((w >> 8) & 0x000f000fu) | k,
-                  ((w >> 12) & 0x000f000fu) | k};
+  const u32x4_t r{(f & m) | k, ((f >> BITS) & m) | k, ((f >> (2 * BITS)) & m) | k, ((f >> (3 * BITS)) & m) | k};
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
 
 
-template <bool GATEUP, int G, int MT>
-__global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
+template <bool GATEUP, int BITS, int G, int MT>
+__global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   constexpr int RB = kAffRB;
   constexpr int HB = GATEUP ? RB / 2 : RB;           // row blocks per matrix per wave
   constexpr int NTILE = 4 * HB * 16;                 // rows per matrix per workgroup
@@ -339,14 +350,28 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
   __shared__ int32_t s_mt[kMaxExperts + 1];
   __shared__ int32_t s_src[MT];
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
-  __shared__ __attribute__((aligned(16))) uint32_t s_bt[4][RB][4][16][4];  // per wave: [rb][block][row][word]
+  // weight macro steps: ROWB bytes of each of a wave's 64 rows
+  constexpr int LPR = BITS == 3 ? 16 : 8;       // lanes per row in one load
+  constexpr int BPL = BITS == 3 ? 12 : 16;      // bytes per lane in one load
+  constexpr int ROWB = LPR * BPL;               // bytes per row per macro step
+  constexpr int SPM = ROWB * 8 / (BITS * kKT);  // K steps per macro step
+  constexpr int RPI = 64 / LPR;                 // rows per load
+  constexpr int NIM = 64 / RPI;                 // loads per macro step
+  constexpr int LSTR = ROWB + 16;               // LDS bytes per row (padded against bank conflicts)
+  constexpr int BW = BPL / 4;
+  static_assert(8 % SPM == 0 && RB * 16 == 64, "macro steps tile the 8-step unrolled rounds and 64 rows");
+  __shared__ __attribute__((aligned(16))) uint32_t s_b[4][64 * LSTR / 4];  // per wave
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int n = a.T * a.k;
   const int rows = a.m0.rows, cols = a.m0.cols;
   Tile t;
   if (!tile_of_block<MT>(a, rows / NTILE, s_off, s_mt, t)) return;
-  const int e = t.e, p0 = t.p0, count = t.count, ntile = t.ntile;
+  // tile coordinates are wave-uniform: keep them (and the addresses built
+  // from them) in scalar registers
+  const int e = __builtin_amdgcn_readfirstlane(t.e), p0 = __builtin_amdgcn_readfirstlane(t.p0);
+  const int count = __builtin_amdgcn_readfirstlane(t.count), ntile = __builtin_amdgcn_readfirstlane(t.ntile);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if (tid < MT) {
     const int p = p0 + min(tid, count - 1);
     s_src[tid] = GATEUP ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
@@ -373,53 +398,98 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
       *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row[i]][a_chunk * 8]) = interleave_halves(ar[i]);
   };
 
-  // weights: lane (g, r16) of block rb reads 16 bytes (inputs 32 g .. + 31)
-  // of row rbase + 16 (rb % HB) + r16 of gate (rb < HB) or up (rb >= HB)
+  // weights: wave row R (0..63) is row rbase0 + 16 (R / 16 % HB) + R % 16 of
+  // gate (R / 16 < HB) or up; load i of a macro step covers wave rows
+  // RPI i .. + RPI - 1, lane l reading BPL bytes at byte (l % LPR) BPL of row
+  // RPI i + l / LPR.
   const QMat w0 = expert_slice(a.m0, e);
   const QMat w1 = expert_slice(a.m1, e);
   const int g = lane >> 4, r16 = lane & 15;
-  const int rbase = ntile * NTILE + wave * HB * 16 + r16;
-  const size_t rw = static_cast<size_t>(w0.row_words), rg = static_cast<size_t>(w0.row_groups);
-  const uint32_t* c0 = w0.codes + static_cast<size_t>(rbase) * rw + 4 * g;
-  const uint32_t* c1 = w1.codes + static_cast<size_t>(rbase) * rw + 4 * g;
-  const uint16_t* s0p = static_cast<const uint16_t*>(w0.scales) + static_cast<size_t>(rbase) * rg;
-  const uint16_t* s1p = static_cast<const uint16_t*>(w1.scales) + static_cast<size_t>(rbase) * rg;
-  const uint16_t* b0p = w0.biases + static_cast<size_t>(rbase) * rg;
-  const uint16_t* b1p = w1.biases + static_cast<size_t>(rbase) * rg;
-  const size_t cstep = 16 * rw, gstep = 16 * rg;
+  const int rbase0 = ntile * NTILE + wave_u * HB * 16;
+  const int rbase = rbase0 + r16;
+  const int rg = w0.row_groups, row_bytes = w0.row_words * 4;
+  const int lrow = lane / LPR, lbyte = (lane % LPR) * BPL;
+  // wave-uniform bases (rows rbase0 ..) and 32-bit lane offsets
+  const char* cb0 = reinterpret_cast<const char*>(w0.codes) + static_cast<size_t>(rbase0) * row_bytes;
+  const char* cb1 = reinterpret_cast<const char*>(w1.codes) + static_cast<size_t>(rbase0) * row_bytes;
+  const uint16_t* s0p = static_cast<const uint16_t*>(w0.scales) + static_cast<size_t>(rbase0) * rg;
+  const uint16_t* s1p = static_cast<const uint16_t*>(w1.scales) + static_cast<size_t>(rbase0) * rg;
+  const uint16_t* b0p = w0.biases + static_cast<size_t>(rbase0) * rg;
+  const uint16_t* b1p = w1.biases + static_cast<size_t>(rbase0) * rg;
+  const uint32_t lrow_off = static_cast<uint32_t>(lrow * row_bytes), sc_off = static_cast<uint32_t>(r16 * rg);
   const int nsteps = cols / kKT;
 
-  auto load_b = [&](u32x4_t (&bq)[RB], int k0) {
+  uint32_t stg[NIM][BW];
+  // the macro step that starts at K step ks (past the end: clamped, unused)
+  auto load_macro = [&](int ks) {
+    const uint32_t o = lrow_off + min((ks / SPM) * ROWB + lbyte, row_bytes - BPL);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const uint32_t* cp = (rb >= HB ? c1 : c0) + (rb % HB) * cstep + k0 / 8;
-      bq[rb] = *reinterpret_cast<const u32x4_t*>(cp);
+    for (int i = 0; i < NIM; ++i) {
+      const int rb = RPI * i / 16;
+      const char* p = (rb >= HB ? cb1 : cb0) + static_cast<size_t>(16 * (rb % HB) + RPI * i % 16) * row_bytes + o;
+      if constexpr (BW == 4) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) stg[i][w] = v[w];
+      } else {
+#pragma unroll
+        for (int w = 0; w < BW; ++w) stg[i][w] = reinterpret_cast<const uint32_t*>(p)[w];
+      }
     }
   };
-  // Scales and biases of K steps ks0 .. ks0 + 7: lane group q holds steps
-  // ks0 + 2q and ks0 + 2q + 1, so the 4 lane groups of a row read 8 steps'
-  // values (32 contiguous bytes for groups of 64) with one request per row.
+  char* const sb_w = reinterpret_cast<char*>(&s_b[wave][0]) + lrow * LSTR + lbyte;
+  auto store_macro = [&]() {
+#pragma unroll
+    for (int i = 0; i < NIM; ++i) {
+      char* d = sb_w + RPI * i * LSTR;
+      if constexpr (BW == 4) {
+        *reinterpret_cast<u32x4_t*>(d) = u32x4_t{stg[i][0], stg[i][1], stg[i][2], stg[i][3]};
+      } else {
+#pragma unroll
+        for (int w = 0; w < BW; ++w) reinterpret_cast<uint32_t*>(d)[w] = stg[i][w];
+      }
+    }
+  };
+  // chunk c = 16 jm + 4 s + g of row 16 rb + r16 of the macro step in LDS
+  const char* const sb_r = reinterpret_cast<const char*>(&s_b[wave][0]) + r16 * LSTR;
+  const int g3w = (3 * g) >> 2, g3sh = 8 * ((3 * g) & 3);  // 3-bit: word and bit of chunk g
+  auto read_chunk = [&](int rb, int s, int jm) -> uint32_t {
+    const char* row = sb_r + 16 * rb * LSTR;
+    if constexpr (BITS == 4) {
+      return *reinterpret_cast<const uint32_t*>(row + 4 * (16 * jm + 4 * s + g));
+    } else if constexpr (BITS == 2) {
+      // codes 0..3 in byte 0, 4..7 in byte 1 -> bytes 0 and 2
+      const uint32_t h = *reinterpret_cast<const uint16_t*>(row + 2 * (16 * jm + 4 * s + g));
+      return (h & 0xffu) | ((h << 8) & 0xff0000u);
+    } else {
+      // 24 bits at byte 3 c: funnel-shift from the two words that hold them,
+      // then move codes 4..7 (bits 12..23) up to bit 16
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(row) + 12 * jm + 3 * s + g3w;
+      const uint32_t v = __builtin_amdgcn_alignbit(w[1], w[0], g3sh);
+      return (v & 0xfffu) | ((v << 4) & 0x0fff0000u);
+    }
+  };
+  // Scales and biases of K steps ks0 .. ks0 + 3: lane group q holds step
+  // ks0 + q, so the 4 lane groups of a row read 4 steps' values (contiguous)
+  // with one request per row and array.
   constexpr int SWS = GPS == 1 ? 1 : GPS / 2;  // 32-bit words per row per step
   struct Scales {
-    uint32_t s[RB][2][SWS], b[RB][2][SWS];
+    uint32_t s[RB][SWS], b[RB][SWS];
   };
   auto load_scales = [&](Scales& sc, int ks0) {
+    const int kq = min(ks0 + g, nsteps - 1) * GPS;  // first group of that step
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kq = min(ks0 + 2 * g + h, nsteps - 1) * GPS;  // first group of that step
+    for (int rb = 0; rb < RB; ++rb) {
+      const uint16_t* sp = (rb >= HB ? s1p : s0p) + static_cast<size_t>(16 * (rb % HB)) * rg + (sc_off + kq);
+      const uint16_t* bp = (rb >= HB ? b1p : b0p) + static_cast<size_t>(16 * (rb % HB)) * rg + (sc_off + kq);
+      if constexpr (GPS == 1) {
+        sc.s[rb][0] = *sp;
+        sc.b[rb][0] = *bp;
+      } else {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const uint16_t* sp = (rb >= HB ? s1p : s0p) + (rb % HB) * gstep + kq;
-        const uint16_t* bp = (rb >= HB ? b1p : b0p) + (rb % HB) * gstep + kq;
-        if constexpr (GPS == 1) {
-          sc.s[rb][h][0] = *sp;
-          sc.b[rb][h][0] = *bp;
-        } else {
-#pragma unroll
-          for (int w = 0; w < SWS; ++w) {
-            sc.s[rb][h][w] = reinterpret_cast<const uint32_t*>(sp)[w];
-            sc.b[rb][h][w] = reinterpret_cast<const uint32_t*>(bp)[w];
-          }
+        for (int w = 0; w < SWS; ++w) {
+          sc.s[rb][w] = reinterpret_cast<const uint32_t*>(sp)[w];
+          sc.b[rb][w] = reinterpret_cast<const uint32_t*>(bp)[w];
         }
       }
     }
@@ -434,38 +504,40 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
   const int valid_mb = min(MB, (count + 15) / 16);
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   u32x4_t a_reg0[ACH], a_reg1[ACH];
-  u32x4_t b_reg0[RB], b_reg1[RB];
   Scales sc_cur, sc_nxt;
 
   auto kloop = [&](auto nmb_tag) {
     constexpr int NMB = decltype(nmb_tag)::value;
-    // step ks = round base + J; weights one step ahead, activations two
-    auto step = [&](int ks, auto j_tag, u32x4_t (&a_ld)[ACH], const u32x4_t (&a_st)[ACH],
-                    const u32x4_t (&b_use)[RB], u32x4_t (&b_ld)[RB]) {
+    // step ks = round base + J; weights one macro step ahead, activations
+    // two steps ahead
+    auto step = [&](int ks, auto j_tag, u32x4_t (&a_ld)[ACH], const u32x4_t (&a_st)[ACH]) {
       constexpr int J = decltype(j_tag)::value;
+      constexpr int JM = J % SPM;
       const int buf = ks & 1;
-      load_b(b_ld, min(ks + 1, nsteps - 1) * kKT);
+      if constexpr (JM == 0) {
+        // a macro step begins: its staged codes go to the wave's LDS slot and
+        // the next macro step's loads are issued
+        store_macro();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+        load_macro(ks + SPM);
+      }
       load_a(a_ld, min(ks + 2, nsteps - 1) * kKT);
-      if constexpr (J == 0) load_scales(sc_nxt, ks + 8);
-      // transpose the step's code words across the lane groups (own LDS slot)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) *reinterpret_cast<u32x4_t*>(&s_bt[wave][rb][g][r16][0]) = b_use[rb];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+      if constexpr (J % 4 == 0) load_scales(sc_nxt, ks + 4);
       uint32_t qw[RB][4];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qw[rb][s] = s_bt[wave][rb][s][r16][g];
-      // this step's scales and biases live in lane group J / 2, half J % 2
+        for (int s = 0; s < 4; ++s) qw[rb][s] = read_chunk(rb, s, JM);
+      // this step's scales and biases live in lane group J % 4
       uint32_t sw[RB][SWS], bw[RB][SWS];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int w = 0; w < SWS; ++w) {
-          sw[rb][w] = __shfl(sc_cur.s[rb][J & 1][w], (J >> 1) * 16 + r16);
-          bw[rb][w] = __shfl(sc_cur.b[rb][J & 1][w], (J >> 1) * 16 + r16);
+          sw[rb][w] = __shfl(sc_cur.s[rb][w], (J & 3) * 16 + r16);
+          bw[rb][w] = __shfl(sc_cur.b[rb][w], (J & 3) * 16 + r16);
         }
 
       f32x4_t dg[GPS][NMB][RB], xg[GPS][NMB];
@@ -484,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
                 af[mb], ones, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : xg[j][mb], 0, 0, 0);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const bf16x8_t bf = u4_to_bf16x8_offset128(qw[rb][s]);
+            const bf16x8_t bf = chunk_to_bf16x8_offset128<BITS>(qw[rb][s]);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
               dg[j][mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -505,7 +577,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
               acc[mb][rb][i] = fmaf(sc, dg[j][mb][rb][i], fmaf(bc, xg[j][mb][i], acc[mb][rb][i]));
         }
       }
-      if constexpr (J == 7) sc_cur = sc_nxt;
+      if constexpr (J % 4 == 3) sc_cur = sc_nxt;
       store_a(a_st, buf ^ 1);  // after the last step: unused, harmless
       lds_barrier();
     };
@@ -518,29 +590,29 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
     using J6 = std::integral_constant<int, 6>;
     using J7 = std::integral_constant<int, 7>;
     load_scales(sc_cur, 0);
-    load_b(b_reg0, 0);
+    load_macro(0);
     load_a(a_reg0, 0);
     store_a(a_reg0, 0);
     load_a(a_reg0, min(1, nsteps - 1) * kKT);
     lds_barrier();
     int ks = 0;
     for (; ks + 8 <= nsteps; ks += 8) {
-      step(ks, J0{}, a_reg1, a_reg0, b_reg0, b_reg1);
-      step(ks + 1, J1{}, a_reg0, a_reg1, b_reg1, b_reg0);
-      step(ks + 2, J2{}, a_reg1, a_reg0, b_reg0, b_reg1);
-      step(ks + 3, J3{}, a_reg0, a_reg1, b_reg1, b_reg0);
-      step(ks + 4, J4{}, a_reg1, a_reg0, b_reg0, b_reg1);
-      step(ks + 5, J5{}, a_reg0, a_reg1, b_reg1, b_reg0);
-      step(ks + 6, J6{}, a_reg1, a_reg0, b_reg0, b_reg1);
-      step(ks + 7, J7{}, a_reg0, a_reg1, b_reg1, b_reg0);
+      step(ks, J0{}, a_reg1, a_reg0);
+      step(ks + 1, J1{}, a_reg0, a_reg1);
+      step(ks + 2, J2{}, a_reg1, a_reg0);
+      step(ks + 3, J3{}, a_reg0, a_reg1);
+      step(ks + 4, J4{}, a_reg1, a_reg0);
+      step(ks + 5, J5{}, a_reg0, a_reg1);
+      step(ks + 6, J6{}, a_reg1, a_reg0);
+      step(ks + 7, J7{}, a_reg0, a_reg1);
     }
-    if (ks < nsteps) step(ks, J0{}, a_reg1, a_reg0, b_reg0, b_reg1);
-    if (ks + 1 < nsteps) step(ks + 1, J1{}, a_reg0, a_reg1, b_reg1, b_reg0);
-    if (ks + 2 < nsteps) step(ks + 2, J2{}, a_reg1, a_reg0, b_reg0, b_reg1);
-    if (ks + 3 < nsteps) step(ks + 3, J3{}, a_reg0, a_reg1, b_reg1, b_reg0);
-    if (ks + 4 < nsteps) step(ks + 4, J4{}, a_reg1, a_reg0, b_reg0, b_reg1);
-    if (ks + 5 < nsteps) step(ks + 5, J5{}, a_reg0, a_reg1, b_reg1, b_reg0);
-    if (ks + 6 < nsteps) step(ks + 6, J6{}, a_reg1, a_reg0, b_reg0, b_reg1);
+    if (ks < nsteps) step(ks, J0{}, a_reg1, a_reg0);
+    if (ks + 1 < nsteps) step(ks + 1, J1{}, a_reg0, a_reg1);
+    if (ks + 2 < nsteps) step(ks + 2, J2{}, a_reg1, a_reg0);
+    if (ks + 3 < nsteps) step(ks + 3, J3{}, a_reg0, a_reg1);
+    if (ks + 4 < nsteps) step(ks + 4, J4{}, a_reg1, a_reg0);
+    if (ks + 5 < nsteps) step(ks + 5, J5{}, a_reg0, a_reg1);
+    if (ks + 6 < nsteps) step(ks + 6, J6{}, a_reg1, a_reg0);
   };
   if constexpr (MB == 2) {
     if (valid_mb == 2)
@@ -574,17 +646,18 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine4(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-static bool affine4_mfma_ok(const QMat& m) {
-  return m.fmt == 0 && m.bits == 4 && (m.group == 32 || m.group == 64 || m.group == 128);
+static bool affine_mfma_ok(const QMat& m) {
+  // 3-bit codes with groups of 32 exceed the register file in this layout
+  // and stay on the streaming path
+  if (m.bits == 3 && m.group == 32) return false;
+  return m.fmt == 0 && (m.bits == 2 || m.bits == 3 || m.bits == 4) && (m.group == 32 || m.group == 64 || m.group == 128);
 }
 
-bool mfma_supported(const QMat& gate, const QMat& down, int64_t T, int k) {
+bool mfma_supported(const QMat& m, bool gateup, int64_t T, int k) {
   // activation rows are addressed with 32-bit element offsets
-  if (T * k * std::max(gate.cols, down.cols) >= (int64_t{1} << 31)) return false;
-  if (gate.fmt == 1 && down.fmt == 1)
-    return gate.cols % kKT == 0 && down.cols % kKT == 0 && gate.rows % 64 == 0 && down.rows % 128 == 0;
-  return affine4_mfma_ok(gate) && affine4_mfma_ok(down) && gate.cols % kKT == 0 && down.cols % kKT == 0 &&
-         gate.rows % (32 * kAffRB) == 0 && down.rows % (64 * kAffRB) == 0;
+  if (T * k * m.cols >= (int64_t{1} << 31) || m.cols % kKT != 0) return false;
+  if (m.fmt == 1) return m.bits == 4 && m.group == 32 && m.rows % (gateup ? 64 : 128) == 0;
+  return affine_mfma_ok(m) && m.rows % ((gateup ? 32 : 64) * kAffRB) == 0;
 }
 
 static unsigned mfma_grid(int T, int k, int E, int rows, int ntile, int mt) {
@@ -594,20 +667,20 @@ static unsigned mfma_grid(int T, int k, int E, int rows, int ntile, int mt) {
   return static_cast<unsigned>(((pairs + 7) / 8) * 8);
 }
 
-template <bool GATEUP, int MT>
+template <bool GATEUP, int BITS, int MT>
 static void launch_affine(const MfmaArgs& a, hipStream_t s) {
   constexpr int NTILE = (GATEUP ? 32 : 64) * kAffRB;
   const dim3 grid(mfma_grid(a.T, a.k, a.E, a.m0.rows, NTILE, MT));
-  if constexpr (MT == 16) {
+  if constexpr (MT == 16 && BITS != 3) {
     if (a.m0.group == 32) {
-      QSMOE_LAUNCH((k_mfma_affine4<GATEUP, 32, 16>), grid, dim3(256), 0, s, a);
+      QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 32, 16>), grid, dim3(256), 0, s, a);
       return;
     }
   }
   if (a.m0.group == 64)
-    QSMOE_LAUNCH((k_mfma_affine4<GATEUP, 64, MT>), grid, dim3(256), 0, s, a);
+    QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 64, MT>), grid, dim3(256), 0, s, a);
   else
-    QSMOE_LAUNCH((k_mfma_affine4<GATEUP, 128, MT>), grid, dim3(256), 0, s, a);
+    QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 128, MT>), grid, dim3(256), 0, s, a);
 }
 
 template <bool GATEUP>
@@ -626,10 +699,14 @@ static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
       QSMOE_LAUNCH((k_mfma_mxfp4<GATEUP, 128, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NT2, 128)),
                          dim3(256), 0, s, a);
     }
+  } else if (m.bits == 2) {
+    launch_affine<GATEUP, 2, 16>(a, s);
+  } else if (m.bits == 3) {
+    launch_affine<GATEUP, 3, 16>(a, s);
   } else if (static_cast<int64_t>(a.T) * a.k < 16LL * a.E || m.group == 32) {
-    launch_affine<GATEUP, 16>(a, s);  // buckets average under 16 tokens (or 4 groups per step)
+    launch_affine<GATEUP, 4, 16>(a, s);  // buckets average under 16 tokens (or 4 groups per step)
   } else {
-    launch_affine<GATEUP, 32>(a, s);
+    launch_affine<GATEUP, 4, 32>(a, s);
   }
   return hipGetLastError();
 }

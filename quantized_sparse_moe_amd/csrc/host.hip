@@ -205,6 +205,11 @@ moe_status run_route(const moe_router& r, const uint16_t* x, const int32_t* toke
       mark(launch_router_topk(logits, r.bias, T, r.num_experts, r.top_k, r.routed_scale, ids, w, s), "router_topk", s));
 }
 
+bool mfma_worthwhile(const QMat& m, int T, int k, int E) {
+  const int64_t per_expert = m.fmt == 0 && m.bits < 4 ? 1 : 4;
+  return static_cast<int64_t>(T) * k >= per_expert * E;
+}
+
 moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const uint16_t* x, int T, int k, int E,
                    const int32_t* offsets, const int32_t* perm, float* y_slot, float* y_sh, uint16_t* h,
                    uint16_t* h_sh, hipStream_t s) {
@@ -212,11 +217,15 @@ moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const u
     GateUpArgs g{to_qmat(shared->gate), to_qmat(shared->up), x, T, k, 1, nullptr, nullptr, 1, h_sh};
     if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) return MOE_ERR_HIP;
   }
-  // Grouped GEMM on the matrix cores once buckets average 4+ tokens.
-  const bool mfma = mfma_supported(to_qmat(routed.gate), to_qmat(routed.down), T, k) &&
-                    static_cast<int64_t>(T) * k >= 4LL * E;
+  // Grouped GEMM on the matrix cores once buckets average enough tokens
+  // (measured crossovers: 4 per expert for 4-bit codes, 1 for 2- and 3-bit,
+  // whose GEMV decode costs more per byte); each projection picks its own
+  // path (both keep h in bucket order).
+  const QMat qg = to_qmat(routed.gate), qd = to_qmat(routed.down);
+  const bool mfma_gu = mfma_worthwhile(qg, T, k, E) && mfma_supported(qg, true, T, k);
+  const bool mfma_dn = mfma_worthwhile(qd, T, k, E) && mfma_supported(qd, false, T, k);
   GateUpArgs g{to_qmat(routed.gate), to_qmat(routed.up), x, T, k, E, offsets, perm, 0, h};
-  if (mfma) {
+  if (mfma_gu) {
     if (mark(launch_mfma_gateup(g, s), "routed_gateup_mfma", s) != hipSuccess) return MOE_ERR_HIP;
   } else if (mark(launch_gateup(g, s), "routed_gateup", s) != hipSuccess) {
     return MOE_ERR_HIP;
@@ -226,7 +235,7 @@ moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const u
     if (mark(launch_down(dn, s), "shared_down", s) != hipSuccess) return MOE_ERR_HIP;
   }
   DownArgs dn{to_qmat(routed.down), h, T, k, E, offsets, perm, 0, y_slot};
-  if (mfma) return hip_status(mark(launch_mfma_down(dn, s), "routed_down_mfma", s));
+  if (mfma_dn) return hip_status(mark(launch_mfma_down(dn, s), "routed_down_mfma", s));
   return hip_status(mark(launch_down(dn, s), "routed_down", s));
 }
 

@@ -77,7 +77,7 @@ struct DownArgs {
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
 // Experts (MFMA grouped GEMM path: many tokens per expert, MXFP4) ------------
-bool mfma_supported(const QMat& gate, const QMat& down, int64_t T, int k);
+bool mfma_supported(const QMat& m, bool gateup, int64_t T, int k);
 hipError_t launch_mfma_gateup(const GateUpArgs& a, hipStream_t s);
 hipError_t launch_mfma_down(const DownArgs& a, hipStream_t s);
 

@@ -143,6 +143,40 @@ def test_deterministic_with_poisoned_workspace():
     assert qm.device_error(ws) == 0
 
 
+@pytest.mark.parametrize("cfg,expect", [
+    (variant("decode", "disp_dec", 213, T=2, d=512, I=256, E=32, I_shared=256),
+     ["dec_router", "dec_gateup", "dec_down_combine"]),
+    (variant("mixed", "disp_mixed_gemv", 214, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
+     ["router_logits", "router_topk", "permute", "shared_gateup", "routed_gateup", "shared_down", "routed_down",
+      "combine"]),
+    (variant("mixed", "disp_mixed_mfma", 215, T=64, d=512, I=256, E=16, top_k=4, I_shared=256),
+     ["router_logits", "router_topk", "permute", "shared_gateup", "routed_gateup_mfma", "shared_down",
+      "routed_down_mfma", "combine"]),
+    (variant("hash", "disp_hash_gemv", 216, T=40, d=512, I=256, E=64, vocab=1000),
+     ["router_hash", "permute", "routed_gateup", "routed_down", "combine"]),
+    (variant("prefill", "disp_mxfp4", 217, T=64, d=512, I=256, E=8, top_k=2, bias_kind="normal"),
+     ["router_logits", "router_topk", "permute", "routed_gateup_mfma", "routed_down_mfma", "combine"]),
+], ids=lambda v: v.name if hasattr(v, "name") else "")
+def test_dispatch_picks_expected_kernels(cfg, expect):
+    """Which kernels a step runs: the fused path for up to 4 top-k tokens; the
+    streaming GEMV under one token per expert (2/3-bit) or four (4-bit); the
+    matrix-core grouped GEMM above that."""
+    layer = synth.gen_layer(cfg)
+    dl = qm.DeviceLayer.from_host(layer)
+    x = xdev(synth.gen_x(cfg, 0))
+    tok = synth.gen_token_ids(cfg, 0)
+    tok = None if tok is None else torch.from_numpy(tok).to("cuda")
+    ws = dl.workspace(cfg.T)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(32)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    names = qm.forward_probed(dl, x, tok, out, ws, evs)
+    torch.cuda.synchronize()
+    assert names == expect
+
+
 def test_forward_probed_matches_forward_and_times_each_kernel():
     """The probed step gives the same output; every kernel gets its own event
     pair with a positive duration, and a too-short event list is rejected."""

@@ -41,6 +41,17 @@ SMALL = [
     variant("prefill", "aff4_g64_mfma_shared", 114, T=80, d=768, I=384, E=16, top_k=4, bias_kind="normal",
             gate_up=FormatSpec("affine", 4, 64), down=FormatSpec("affine", 4, 64),
             shared=FormatSpec("affine", 8, 64), I_shared=128),
+    # 2- and 3-bit codes on the matrix cores (4+ tokens per expert)
+    variant("mixed", "aff2_3_mfma", 115, T=64, d=512, I=256, E=16, top_k=4, bias_kind="normal",
+            gate_up=FormatSpec("affine", 2, 128), down=FormatSpec("affine", 3, 64),
+            shared=FormatSpec("affine", 8, 64), I_shared=256),
+    # (K = 768 and 384: the last 4-step weight block of a row is partial)
+    variant("mixed", "aff3g64_2g128_mfma", 116, T=37, d=768, I=384, E=8, top_k=3, bias_kind="normal",
+            gate_up=FormatSpec("affine", 3, 64), down=FormatSpec("affine", 2, 128)),
+    variant("mixed", "aff4g32_3g32_mixed_paths", 118, T=40, d=512, I=256, E=8, top_k=2, bias_kind="normal",
+            gate_up=FormatSpec("affine", 4, 32), down=FormatSpec("affine", 3, 32)),
+    # 2- and 3-bit codes on the streaming GEMV (under one token per expert)
+    variant("mixed", "mixed_gemv", 117, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
 ]
 
 
