@@ -50,10 +50,13 @@ struct MfmaArgs {
   QMat m0, m1;             // gate, up (GATEUP) or down
   const uint16_t* x;       // gate/up: activations [T][cols]; down: h [T*k][cols] (bucketed order)
   int32_t T, k, E;
-  const int32_t* offsets;
-  const int32_t* perm;
+  const int32_t* offsets;  // routed only
+  const int32_t* perm;     // routed only
+  int32_t shared;          // one expert over all T tokens in token order (k = E = 1)
   uint16_t* h;             // gate/up output [T*k][I]
   float* y;                // down output [T*k][d] (assignment order)
+  int32_t ksplit;          // K slices (affine only); > 1: fp32 partial sums to part
+  float* part;             // [ksplit][T*k][2 I] (gate/up: g then u) or [ksplit][T*k][d]
 };
 
 __device__ __forceinline__ bf16x8_t fp4_to_bf16x8(uint32_t word, float scale) {
@@ -73,14 +76,14 @@ __device__ __forceinline__ bf16x8_t fp4_to_bf16x8(uint32_t word, float scale) {
 // weights run on the same L2. Returns false (for the whole workgroup) when
 // the grid's upper bound left this workgroup without a pair.
 struct Tile {
-  int e, p0, count, ntile;
+  int e, p0, count, ntile, kslice;
 };
 
 template <int MT>
 __device__ bool tile_of_block(const MfmaArgs& a, int n_ntiles, int32_t* s_off, int32_t* s_mt, Tile& t) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int n = a.T * a.k;
-  for (int i = tid; i <= a.E; i += 256) s_off[i] = min(max(a.offsets[i], 0), n);
+  for (int i = tid; i <= a.E; i += 256) s_off[i] = a.shared ? (i == 0 ? 0 : n) : min(max(a.offsets[i], 0), n);
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -99,14 +102,26 @@ __device__ bool tile_of_block(const MfmaArgs& a, int n_ntiles, int32_t* s_off, i
     if (lane == 0) s_mt[a.E] = carry;
   }
   __syncthreads();
-  const int64_t pairs = static_cast<int64_t>(s_mt[a.E]) * n_ntiles;
+  const int ks = max(a.ksplit, 1);
+  const int64_t pairs = static_cast<int64_t>(s_mt[a.E]) * n_ntiles * ks;
   const int64_t per_xcd = (pairs + 7) / 8;
   const int64_t local = blockIdx.x / 8;
   if (local >= per_xcd) return false;
   const int64_t pair = (blockIdx.x % 8) * per_xcd + local;
   if (pair >= pairs) return false;
-  const int mtile = static_cast<int>(pair / n_ntiles);
-  t.ntile = static_cast<int>(pair % n_ntiles);
+  int mtile;
+  if (ks == 1) {
+    mtile = static_cast<int>(pair / n_ntiles);
+    t.ntile = static_cast<int>(pair % n_ntiles);
+    t.kslice = 0;
+  } else {
+    // K-split: the m-tiles of one (n-tile, K slice) weight block are adjacent
+    const int64_t mt = s_mt[a.E];
+    mtile = static_cast<int>(pair % mt);
+    const int64_t wb = pair / mt;
+    t.ntile = static_cast<int>(wb / ks);
+    t.kslice = static_cast<int>(wb % ks);
+  }
   int e = 0;
   for (int e0 = 0; e0 < a.E; e0 += 64) {
     const int ee = e0 + lane;
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   const int e = t.e, p0 = t.p0, count = t.count, ntile = t.ntile;
   if (tid < MT) {
     const int p = p0 + min(tid, count - 1);
-    s_src[tid] = GATEUP ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
+    s_src[tid] = GATEUP && !a.shared ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
   }
   __syncthreads();
 
@@ -277,7 +292,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
         for (int rb = 0; rb < HB; ++rb)
           hrow[rb * 16] = static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][rb][i]) * acc[mb][rb + HB][i]));
       } else {
-        const int slot = min(max(a.perm[p0 + tl], 0), n - 1);
+        const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
         float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) yrow[rb * 16] = acc[mb][rb][i];
@@ -324,14 +339,29 @@ __device__ __forceinline__ u32x4_t interleave_halves(const u32x4_t& v) {
                  (v[1] & 0xffffu) | (v[3] << 16), (v[1] >> 16) | (v[3] & 0xffff0000u)};
 }
 
-// The chunk word f (code i at bit BITS i, code i + 4 at bit 16 + BITS i) as
-// the bf16 pairs (128 + q_i, 128 + q_{i+4}), i = 0..3.
+// A chunk of 8 codes as the bf16 pairs (v_i, v_{i+4}), i = 0..3, where v is
+// 128 + q for 2-, 3- and 4-bit codes (chunk word: code i at bit BITS i, code
+// i + 4 at bit 16 + BITS i) and q itself for 8-bit codes (two words, code i
+// in byte i % 4 of word i / 4; the byte converts exactly to fp32, whose top
+// half is the exact bf16).
 template <int BITS>
-__device__ __forceinline__ bf16x8_t chunk_to_bf16x8_offset128(uint32_t f) {
-  constexpr uint32_t m = ((1u << BITS) - 1u) * 0x10001u;
-  const uint32_t k = bf16x2_128();
-  const u32x4_t r{(f & m) | k, ((f >> BITS) & m) | k, ((f >> (2 * BITS)) & m) | k, ((f >> (3 * BITS)) & m) | k};
-  return __builtin_bit_cast(bf16x8_t, r);
+__device__ __forceinline__ bf16x8_t chunk_to_bf16x8(const uint32_t (&f)[BITS == 8 ? 2 : 1]) {
+  if constexpr (BITS == 8) {
+    u32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = static_cast<float>((f[0] >> (8 * i)) & 0xffu);
+      const float hi = static_cast<float>((f[1] >> (8 * i)) & 0xffu);
+      r[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    }
+    return __builtin_bit_cast(bf16x8_t, r);
+  } else {
+    constexpr uint32_t m = ((1u << BITS) - 1u) * 0x10001u;
+    const uint32_t k = bf16x2_128();
+    const uint32_t w = f[0];
+    const u32x4_t r{(w & m) | k, ((w >> BITS) & m) | k, ((w >> (2 * BITS)) & m) | k, ((w >> (3 * BITS)) & m) | k};
+    return __builtin_bit_cast(bf16x8_t, r);
+  }
 }
 
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
@@ -351,6 +381,8 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   __shared__ int32_t s_src[MT];
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
   // weight macro steps: ROWB bytes of each of a wave's 64 rows
+  constexpr int QW = BITS == 8 ? 2 : 1;         // words per 8-code chunk as read
+  constexpr float kOff = BITS == 8 ? 0.0f : 128.0f;  // value of code 0 as decoded
   constexpr int LPR = BITS == 3 ? 16 : 8;       // lanes per row in one load
   constexpr int BPL = BITS == 3 ? 12 : 16;      // bytes per lane in one load
   constexpr int ROWB = LPR * BPL;               // bytes per row per macro step
@@ -371,10 +403,11 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   // from them) in scalar registers
   const int e = __builtin_amdgcn_readfirstlane(t.e), p0 = __builtin_amdgcn_readfirstlane(t.p0);
   const int count = __builtin_amdgcn_readfirstlane(t.count), ntile = __builtin_amdgcn_readfirstlane(t.ntile);
+  const int kslice = __builtin_amdgcn_readfirstlane(t.kslice);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   if (tid < MT) {
     const int p = p0 + min(tid, count - 1);
-    s_src[tid] = GATEUP ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
+    s_src[tid] = GATEUP && !a.shared ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
   }
   __syncthreads();
 
@@ -418,6 +451,10 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   const uint16_t* b1p = w1.biases + static_cast<size_t>(rbase0) * rg;
   const uint32_t lrow_off = static_cast<uint32_t>(lrow * row_bytes), sc_off = static_cast<uint32_t>(r16 * rg);
   const int nsteps = cols / kKT;
+  // this workgroup's K steps [ks_begin, ks_end) (the host makes slices a
+  // multiple of SPM steps)
+  const int slice = nsteps / max(a.ksplit, 1);
+  const int ks_begin = kslice * slice, ks_end = ks_begin + slice;
 
   uint32_t stg[NIM][BW];
   // the macro step that starts at K step ks (past the end: clamped, unused)
@@ -453,20 +490,24 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   // chunk c = 16 jm + 4 s + g of row 16 rb + r16 of the macro step in LDS
   const char* const sb_r = reinterpret_cast<const char*>(&s_b[wave][0]) + r16 * LSTR;
   const int g3w = (3 * g) >> 2, g3sh = 8 * ((3 * g) & 3);  // 3-bit: word and bit of chunk g
-  auto read_chunk = [&](int rb, int s, int jm) -> uint32_t {
+  auto read_chunk = [&](int rb, int s, int jm, uint32_t (&c)[QW]) {
     const char* row = sb_r + 16 * rb * LSTR;
-    if constexpr (BITS == 4) {
-      return *reinterpret_cast<const uint32_t*>(row + 4 * (16 * jm + 4 * s + g));
+    if constexpr (BITS == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + 8 * (16 * jm + 4 * s + g));
+      c[0] = v.x;
+      c[QW - 1] = v.y;
+    } else if constexpr (BITS == 4) {
+      c[0] = *reinterpret_cast<const uint32_t*>(row + 4 * (16 * jm + 4 * s + g));
     } else if constexpr (BITS == 2) {
       // codes 0..3 in byte 0, 4..7 in byte 1 -> bytes 0 and 2
       const uint32_t h = *reinterpret_cast<const uint16_t*>(row + 2 * (16 * jm + 4 * s + g));
-      return (h & 0xffu) | ((h << 8) & 0xff0000u);
+      c[0] = (h & 0xffu) | ((h << 8) & 0xff0000u);
     } else {
       // 24 bits at byte 3 c: funnel-shift from the two words that hold them,
       // then move codes 4..7 (bits 12..23) up to bit 16
       const uint32_t* w = reinterpret_cast<const uint32_t*>(row) + 12 * jm + 3 * s + g3w;
       const uint32_t v = __builtin_amdgcn_alignbit(w[1], w[0], g3sh);
-      return (v & 0xfffu) | ((v << 4) & 0x0fff0000u);
+      c[0] = (v & 0xfffu) | ((v << 4) & 0x0fff0000u);
     }
   };
   // Scales and biases of K steps ks0 .. ks0 + 3: lane group q holds step
@@ -525,11 +566,11 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
       }
       load_a(a_ld, min(ks + 2, nsteps - 1) * kKT);
       if constexpr (J % 4 == 0) load_scales(sc_nxt, ks + 4);
-      uint32_t qw[RB][4];
+      uint32_t qw[RB][4][QW];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qw[rb][s] = read_chunk(rb, s, JM);
+        for (int s = 0; s < 4; ++s) read_chunk(rb, s, JM, qw[rb][s]);
       // this step's scales and biases live in lane group J % 4
       uint32_t sw[RB][SWS], bw[RB][SWS];
 #pragma unroll
@@ -540,7 +581,24 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
           bw[rb][w] = __shfl(sc_cur.b[rb][w], (J & 3) * 16 + r16);
         }
 
+      // group j's scale and bias applied to its partial tiles: after all
+      // groups' MFMAs (more independent work between an MFMA and its use), or
+      // right after each group's when two m-blocks of several groups would
+      // not fit the register file
+      constexpr bool EPI_EACH = NMB == 2 && GPS >= 2;
       f32x4_t dg[GPS][NMB][RB], xg[GPS][NMB];
+      auto epilogue = [&](int j) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const float sc = f16_to_f32(static_cast<uint16_t>(sw[rb][j / 2] >> (16 * (j & 1))));
+          const float bc = fmaf(-kOff, sc, f16_to_f32(static_cast<uint16_t>(bw[rb][j / 2] >> (16 * (j & 1)))));
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[mb][rb][i] = fmaf(sc, dg[j][mb][rb][i], fmaf(bc, xg[j][mb][i], acc[mb][rb][i]));
+        }
+      };
 #pragma unroll
       for (int j = 0; j < GPS; ++j) {
 #pragma unroll
@@ -556,26 +614,18 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
                 af[mb], ones, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : xg[j][mb], 0, 0, 0);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const bf16x8_t bf = chunk_to_bf16x8_offset128<BITS>(qw[rb][s]);
+            const bf16x8_t bf = chunk_to_bf16x8<BITS>(qw[rb][s]);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
               dg[j][mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   af[mb], bf, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : dg[j][mb][rb], 0, 0, 0);
           }
         }
+        if constexpr (EPI_EACH) epilogue(j);
       }
+      if constexpr (!EPI_EACH) {
 #pragma unroll
-      for (int j = 0; j < GPS; ++j) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float sc = f16_to_f32(static_cast<uint16_t>(sw[rb][j / 2] >> (16 * (j & 1))));
-          const float bc = fmaf(-128.0f, sc, f16_to_f32(static_cast<uint16_t>(bw[rb][j / 2] >> (16 * (j & 1)))));
-#pragma unroll
-          for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[mb][rb][i] = fmaf(sc, dg[j][mb][rb][i], fmaf(bc, xg[j][mb][i], acc[mb][rb][i]));
-        }
+        for (int j = 0; j < GPS; ++j) epilogue(j);
       }
       if constexpr (J % 4 == 3) sc_cur = sc_nxt;
       store_a(a_st, buf ^ 1);  // after the last step: unused, harmless
@@ -589,14 +639,14 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
     using J5 = std::integral_constant<int, 5>;
     using J6 = std::integral_constant<int, 6>;
     using J7 = std::integral_constant<int, 7>;
-    load_scales(sc_cur, 0);
-    load_macro(0);
-    load_a(a_reg0, 0);
+    load_scales(sc_cur, ks_begin);
+    load_macro(ks_begin);
+    load_a(a_reg0, ks_begin * kKT);
     store_a(a_reg0, 0);
-    load_a(a_reg0, min(1, nsteps - 1) * kKT);
+    load_a(a_reg0, min(ks_begin + 1, nsteps - 1) * kKT);
     lds_barrier();
-    int ks = 0;
-    for (; ks + 8 <= nsteps; ks += 8) {
+    int ks = ks_begin;
+    for (; ks + 8 <= ks_end; ks += 8) {
       step(ks, J0{}, a_reg1, a_reg0);
       step(ks + 1, J1{}, a_reg0, a_reg1);
       step(ks + 2, J2{}, a_reg1, a_reg0);
@@ -606,13 +656,13 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
       step(ks + 6, J6{}, a_reg1, a_reg0);
       step(ks + 7, J7{}, a_reg0, a_reg1);
     }
-    if (ks < nsteps) step(ks, J0{}, a_reg1, a_reg0);
-    if (ks + 1 < nsteps) step(ks + 1, J1{}, a_reg0, a_reg1);
-    if (ks + 2 < nsteps) step(ks + 2, J2{}, a_reg1, a_reg0);
-    if (ks + 3 < nsteps) step(ks + 3, J3{}, a_reg0, a_reg1);
-    if (ks + 4 < nsteps) step(ks + 4, J4{}, a_reg1, a_reg0);
-    if (ks + 5 < nsteps) step(ks + 5, J5{}, a_reg0, a_reg1);
-    if (ks + 6 < nsteps) step(ks + 6, J6{}, a_reg1, a_reg0);
+    if (ks < ks_end) step(ks, J0{}, a_reg1, a_reg0);
+    if (ks + 1 < ks_end) step(ks + 1, J1{}, a_reg0, a_reg1);
+    if (ks + 2 < ks_end) step(ks + 2, J2{}, a_reg1, a_reg0);
+    if (ks + 3 < ks_end) step(ks + 3, J3{}, a_reg0, a_reg1);
+    if (ks + 4 < ks_end) step(ks + 4, J4{}, a_reg1, a_reg0);
+    if (ks + 5 < ks_end) step(ks + 5, J5{}, a_reg0, a_reg1);
+    if (ks + 6 < ks_end) step(ks + 6, J6{}, a_reg1, a_reg0);
   };
   if constexpr (MB == 2) {
     if (valid_mb == 2)
@@ -630,13 +680,19 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int tl = mb * 16 + 4 * g + i;
       if (tl >= count) continue;
-      if constexpr (GATEUP) {
+      if (a.ksplit > 1) {
+        // partial sums of this K slice, reduced in slice order by the finisher
+        const int width = GATEUP ? 2 * rows : rows;
+        float* prow = a.part + (static_cast<size_t>(kslice) * n + (p0 + tl)) * width + rbase;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) prow[(GATEUP && rb >= HB ? rows : 0) + (rb % HB) * 16] = acc[mb][rb][i];
+      } else if constexpr (GATEUP) {
         uint16_t* hrow = a.h + static_cast<size_t>(p0 + tl) * rows + rbase;
 #pragma unroll
         for (int rb = 0; rb < HB; ++rb)
           hrow[rb * 16] = static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mb][rb][i]) * acc[mb][rb + HB][i]));
       } else {
-        const int slot = min(max(a.perm[p0 + tl], 0), n - 1);
+        const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
         float* yrow = a.y + static_cast<size_t>(slot) * rows + rbase;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) yrow[rb * 16] = acc[mb][rb][i];
@@ -650,7 +706,8 @@ static bool affine_mfma_ok(const QMat& m) {
   // 3-bit codes with groups of 32 exceed the register file in this layout
   // and stay on the streaming path
   if (m.bits == 3 && m.group == 32) return false;
-  return m.fmt == 0 && (m.bits == 2 || m.bits == 3 || m.bits == 4) && (m.group == 32 || m.group == 64 || m.group == 128);
+  return m.fmt == 0 && (m.bits == 2 || m.bits == 3 || m.bits == 4 || m.bits == 8) &&
+         (m.group == 32 || m.group == 64 || m.group == 128);
 }
 
 bool mfma_supported(const QMat& m, bool gateup, int64_t T, int k) {
@@ -660,17 +717,17 @@ bool mfma_supported(const QMat& m, bool gateup, int64_t T, int k) {
   return affine_mfma_ok(m) && m.rows % ((gateup ? 32 : 64) * kAffRB) == 0;
 }
 
-static unsigned mfma_grid(int T, int k, int E, int rows, int ntile, int mt) {
+static unsigned mfma_grid(int T, int k, int E, int rows, int ntile, int mt, int ksplit = 1) {
   const int64_t tk = static_cast<int64_t>(T) * k;
   const int64_t mtiles = (tk + mt - 1) / mt + std::min<int64_t>(tk, E);
-  const int64_t pairs = mtiles * (rows / ntile);
+  const int64_t pairs = mtiles * (rows / ntile) * std::max(ksplit, 1);
   return static_cast<unsigned>(((pairs + 7) / 8) * 8);
 }
 
 template <bool GATEUP, int BITS, int MT>
 static void launch_affine(const MfmaArgs& a, hipStream_t s) {
   constexpr int NTILE = (GATEUP ? 32 : 64) * kAffRB;
-  const dim3 grid(mfma_grid(a.T, a.k, a.E, a.m0.rows, NTILE, MT));
+  const dim3 grid(mfma_grid(a.T, a.k, a.E, a.m0.rows, NTILE, MT, a.ksplit));
   if constexpr (MT == 16 && BITS != 3) {
     if (a.m0.group == 32) {
       QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 32, 16>), grid, dim3(256), 0, s, a);
@@ -704,19 +761,82 @@ static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   } else if (m.bits == 3) {
     launch_affine<GATEUP, 3, 16>(a, s);
   } else if (static_cast<int64_t>(a.T) * a.k < 16LL * a.E || m.group == 32) {
-    launch_affine<GATEUP, 4, 16>(a, s);  // buckets average under 16 tokens (or 4 groups per step)
+    // buckets average under 16 tokens (or 4 groups per step)
+    if (m.bits == 8)
+      launch_affine<GATEUP, 8, 16>(a, s);
+    else
+      launch_affine<GATEUP, 4, 16>(a, s);
+  } else if (m.bits == 8) {
+    launch_affine<GATEUP, 8, 32>(a, s);
   } else {
     launch_affine<GATEUP, 4, 32>(a, s);
   }
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// K-split (shared expert at small T): too few (m-tile, n-tile) pairs to fill
+// the chip, so each pair's K range is split over ksplit workgroups, which
+// write fp32 partial sums; the finishers add the slices in slice order
+// (deterministic), then apply SwiGLU and round h to bf16 (gate/up) or store
+// y (down).
+int mfma_shared_ksplit(const QMat& m, bool gateup, int T) {
+  if (m.fmt != 0) return 1;
+  const int mt = T < 16 ? 16 : (m.bits < 4 || m.group == 32 ? 16 : 32);
+  const int ntile = (gateup ? 32 : 64) * kAffRB;
+  const int pairs = ((T + mt - 1) / mt) * (m.rows / ntile);
+  const int nsteps = m.cols / kKT;
+  int ks = 1;
+  // slices of a multiple of 4 K steps (so of every format's macro step)
+  while (pairs * ks < 256 && nsteps % (ks * 2) == 0 && (nsteps / (ks * 2)) % 4 == 0) ks *= 2;
+  return ks;
+}
+
+__global__ __launch_bounds__(256) void k_swiglu_parts(const float* __restrict__ part, int ks, int n, int I,
+                                                      uint16_t* __restrict__ h) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= static_cast<int64_t>(n) * I) return;
+  const int64_t p = i / I, r = i - p * I;
+  float g = 0.0f, u = 0.0f;
+  for (int s = 0; s < ks; ++s) {
+    const float* row = part + (static_cast<int64_t>(s) * n + p) * 2 * I;
+    g += row[r];
+    u += row[I + r];
+  }
+  h[i] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * u));
+}
+
+__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ part, int ks, int64_t count,
+                                                   float* __restrict__ y) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count) return;
+  float v = 0.0f;
+  for (int s = 0; s < ks; ++s) v += part[static_cast<int64_t>(s) * count + i];
+  y[i] = v;
+}
+
+hipError_t launch_swiglu_parts(const float* part, int ks, int n, int I, uint16_t* h, hipStream_t s) {
+  const int64_t count = static_cast<int64_t>(n) * I;
+  QSMOE_LAUNCH(k_swiglu_parts, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, s, part, ks, n, I, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_parts(const float* part, int ks, int64_t count, float* y, hipStream_t s) {
+  QSMOE_LAUNCH(k_sum_parts, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, s, part, ks, count, y);
+  return hipGetLastError();
+}
+
+// Shared mode (one expert over all tokens) takes k = E = 1.
 hipError_t launch_mfma_gateup(const GateUpArgs& g, hipStream_t s) {
-  return launch_mfma<true>(MfmaArgs{g.gate, g.up, g.x, g.T, g.k, g.E, g.offsets, g.perm, g.h, nullptr}, s);
+  const int k = g.shared ? 1 : g.k, E = g.shared ? 1 : g.E;
+  return launch_mfma<true>(
+      MfmaArgs{g.gate, g.up, g.x, g.T, k, E, g.offsets, g.perm, g.shared, g.h, nullptr, g.ksplit, g.part}, s);
 }
 
 hipError_t launch_mfma_down(const DownArgs& d, hipStream_t s) {
-  return launch_mfma<false>(MfmaArgs{d.down, d.down, d.h, d.T, d.k, d.E, d.offsets, d.perm, nullptr, d.y}, s);
+  const int k = d.shared ? 1 : d.k, E = d.shared ? 1 : d.E;
+  return launch_mfma<false>(
+      MfmaArgs{d.down, d.down, d.h, d.T, k, E, d.offsets, d.perm, d.shared, nullptr, d.y, d.ksplit, d.part}, s);
 }
 
 }  // namespace qsmoe

@@ -3,6 +3,7 @@
 // except moe_device_error, which exists for tests.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -106,14 +107,30 @@ size_t route_ws_bytes(const moe_router& r, int T) {
   return kHeader + (r.mode == MOE_ROUTE_TOPK ? align_up(static_cast<size_t>(T) * r.num_experts * 4) : 0);
 }
 
+// fp32 partial sums of the shared expert's K-split projections, bounded for
+// every token count up to T: the slice count only falls as T grows (it is 1
+// from some T_cap on), so slices(8) * min(T, T_cap) rows always suffice.
+size_t shared_part_bytes(const moe_experts& sh, int T) {
+  auto rows_bound = [T](const QMat& m, bool gateup) -> size_t {
+    const int ks8 = mfma_shared_ksplit(m, gateup, 8);
+    if (ks8 <= 1) return 0;
+    int tcap = 8;
+    while (mfma_shared_ksplit(m, gateup, tcap) > 1) tcap *= 2;
+    return static_cast<size_t>(ks8) * std::min(T, tcap);
+  };
+  const QMat g = to_qmat(sh.gate), dn = to_qmat(sh.down);
+  const size_t a = rows_bound(g, true) * 2 * g.rows * 4, b = rows_bound(dn, false) * dn.rows * 4;
+  return align_up(std::max(a, b));
+}
+
 size_t ffn_ws_bytes(const moe_experts& routed, const moe_experts* shared, int T, int k) {
   size_t b = kHeader + align_up(static_cast<size_t>(T) * k * routed.gate.rows * 2);
-  if (shared) b += align_up(static_cast<size_t>(T) * shared->gate.rows * 2);
+  if (shared) b += align_up(static_cast<size_t>(T) * shared->gate.rows * 2) + shared_part_bytes(*shared, T);
   return b;
 }
 
 struct FwdLayout {
-  size_t ids, w, logits, keys, offsets, perm, h, h_sh, y_slot, y_sh, total;
+  size_t ids, w, logits, keys, offsets, perm, h, h_sh, sh_part, y_slot, y_sh, total;
 };
 
 FwdLayout forward_layout(const moe_layer& L, int T) {
@@ -137,6 +154,8 @@ FwdLayout forward_layout(const moe_layer& L, int T) {
   o += align_up(tk * L.routed.gate.rows * 2);
   f.h_sh = o;
   o += L.shared ? align_up(static_cast<size_t>(T) * L.shared->gate.rows * 2) : 0;
+  f.sh_part = o;
+  o += L.shared ? shared_part_bytes(*L.shared, T) : 0;
   f.y_slot = o;
   o += align_up(tk * d * 4);
   f.y_sh = o;
@@ -212,10 +231,28 @@ bool mfma_worthwhile(const QMat& m, int T, int k, int E) {
 
 moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const uint16_t* x, int T, int k, int E,
                    const int32_t* offsets, const int32_t* perm, float* y_slot, float* y_sh, uint16_t* h,
-                   uint16_t* h_sh, hipStream_t s) {
+                   uint16_t* h_sh, float* sh_part, hipStream_t s) {
+  // The shared expert (every token, token order) is a dense GEMM on the
+  // matrix cores from 8 tokens on (K split over workgroups while its tiles
+  // are too few to fill the chip), a streaming GEMV below that.
+  bool sh_mfma = false;
+  int ks_gu = 1, ks_dn = 1;
   if (shared) {
-    GateUpArgs g{to_qmat(shared->gate), to_qmat(shared->up), x, T, k, 1, nullptr, nullptr, 1, h_sh};
-    if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) return MOE_ERR_HIP;
+    const QMat sg = to_qmat(shared->gate), sd = to_qmat(shared->down);
+    sh_mfma = T >= 8 && mfma_supported(sg, true, T, 1) && mfma_supported(sd, false, T, 1);
+    if (sh_mfma) {
+      ks_gu = mfma_shared_ksplit(sg, true, T);
+      ks_dn = mfma_shared_ksplit(sd, false, T);
+    }
+    GateUpArgs g{sg, to_qmat(shared->up), x, T, k, 1, nullptr, nullptr, 1, h_sh, ks_gu, sh_part};
+    if (sh_mfma) {
+      if (mark(launch_mfma_gateup(g, s), "shared_gateup_mfma", s) != hipSuccess) return MOE_ERR_HIP;
+      if (ks_gu > 1 && mark(launch_swiglu_parts(sh_part, ks_gu, T, sg.rows, h_sh, s), "shared_swiglu", s) !=
+                           hipSuccess)
+        return MOE_ERR_HIP;
+    } else if (mark(launch_gateup(g, s), "shared_gateup", s) != hipSuccess) {
+      return MOE_ERR_HIP;
+    }
   }
   // Grouped GEMM on the matrix cores once buckets average enough tokens
   // (measured crossovers: 4 per expert for 4-bit codes, 1 for 2- and 3-bit,
@@ -231,8 +268,15 @@ moe_status run_ffn(const moe_experts& routed, const moe_experts* shared, const u
     return MOE_ERR_HIP;
   }
   if (shared) {
-    DownArgs dn{to_qmat(shared->down), h_sh, T, k, 1, nullptr, nullptr, 1, y_sh};
-    if (mark(launch_down(dn, s), "shared_down", s) != hipSuccess) return MOE_ERR_HIP;
+    DownArgs dn{to_qmat(shared->down), h_sh, T, k, 1, nullptr, nullptr, 1, y_sh, ks_dn, sh_part};
+    if (sh_mfma) {
+      if (mark(launch_mfma_down(dn, s), "shared_down_mfma", s) != hipSuccess) return MOE_ERR_HIP;
+      if (ks_dn > 1 && mark(launch_sum_parts(sh_part, ks_dn, static_cast<int64_t>(T) * dn.down.rows, y_sh, s),
+                            "shared_sum", s) != hipSuccess)
+        return MOE_ERR_HIP;
+    } else if (mark(launch_down(dn, s), "shared_down", s) != hipSuccess) {
+      return MOE_ERR_HIP;
+    }
   }
   DownArgs dn{to_qmat(routed.down), h, T, k, E, offsets, perm, 0, y_slot};
   if (mfma_dn) return hip_status(mark(launch_mfma_down(dn, s), "routed_down_mfma", s));
@@ -328,8 +372,12 @@ moe_status moe_expert_ffn(const moe_experts* routed, const moe_experts* shared, 
   if (ws == nullptr || ws_bytes < ffn_ws_bytes(*routed, shared, T, k)) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   uint16_t* h = at<uint16_t>(ws, kHeader);
-  uint16_t* h_sh = at<uint16_t>(ws, kHeader + align_up(static_cast<size_t>(T) * k * routed->gate.rows * 2));
-  return run_ffn(*routed, shared, x_bf16, T, k, E, expert_offsets, perm, y_slot, y_shared, h, h_sh, stream);
+  const size_t o_sh = kHeader + align_up(static_cast<size_t>(T) * k * routed->gate.rows * 2);
+  uint16_t* h_sh = at<uint16_t>(ws, o_sh);
+  float* sh_part =
+      shared ? at<float>(ws, o_sh + align_up(static_cast<size_t>(T) * shared->gate.rows * 2)) : nullptr;
+  return run_ffn(*routed, shared, x_bf16, T, k, E, expert_offsets, perm, y_slot, y_shared, h, h_sh, sh_part,
+                 stream);
 }
 
 moe_status moe_combine(const float* y_slot, const float* topk_w, const float* y_shared, int32_t T, int32_t k,
@@ -406,7 +454,7 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
   if (mark(launch_permute(ids, T * k, E, offsets, perm, err, stream), "permute", stream) != hipSuccess)
     return MOE_ERR_HIP;
   if ((s = run_ffn(L.routed, L.shared, x_bf16, T, k, E, offsets, perm, y_slot, y_sh, at<uint16_t>(ws, f.h),
-                   at<uint16_t>(ws, f.h_sh), stream)) != MOE_OK)
+                   at<uint16_t>(ws, f.h_sh), at<float>(ws, f.sh_part), stream)) != MOE_OK)
     return s;
   return hip_status(
       mark(launch_combine(y_slot, w, y_sh, T, k, d, out_dtype == MOE_OUT_F32, out, stream), "combine", stream));

@@ -62,6 +62,8 @@ struct GateUpArgs {
   const int32_t* perm;     // routed only
   int32_t shared;
   uint16_t* h;             // bf16 [T*k][I] in bucketed order (routed) or [T][I] (shared)
+  int32_t ksplit = 1;      // MFMA path only: > 1 writes fp32 partials to part instead of h
+  float* part = nullptr;
 };
 hipError_t launch_gateup(const GateUpArgs& a, hipStream_t s);
 
@@ -73,11 +75,18 @@ struct DownArgs {
   const int32_t* perm;
   int32_t shared;
   float* y;                // fp32 [T*k][d] in assignment order (routed) or [T][d] (shared)
+  int32_t ksplit = 1;      // MFMA path only: > 1 writes fp32 partials to part instead of y
+  float* part = nullptr;
 };
 hipError_t launch_down(const DownArgs& a, hipStream_t s);
 
 // Experts (MFMA grouped GEMM path: many tokens per expert, MXFP4) ------------
 bool mfma_supported(const QMat& m, bool gateup, int64_t T, int k);
+// K slices for the shared expert's projection at T tokens (1: no split), and
+// the finishers of a split: h = bf16(silu(sum g) * sum u), y = sum of slices.
+int mfma_shared_ksplit(const QMat& m, bool gateup, int T);
+hipError_t launch_swiglu_parts(const float* part, int ks, int n, int I, uint16_t* h, hipStream_t s);
+hipError_t launch_sum_parts(const float* part, int ks, int64_t count, float* y, hipStream_t s);
 hipError_t launch_mfma_gateup(const GateUpArgs& a, hipStream_t s);
 hipError_t launch_mfma_down(const DownArgs& a, hipStream_t s);
 

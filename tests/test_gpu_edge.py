@@ -147,11 +147,17 @@ def test_deterministic_with_poisoned_workspace():
     (variant("decode", "disp_dec", 213, T=2, d=512, I=256, E=32, I_shared=256),
      ["dec_router", "dec_gateup", "dec_down_combine"]),
     (variant("mixed", "disp_mixed_gemv", 214, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
+     ["router_logits", "router_topk", "permute", "shared_gateup_mfma", "routed_gateup", "shared_down_mfma",
+      "routed_down", "combine"]),
+    (variant("mixed", "disp_mixed_mfma", 215, T=64, d=512, I=256, E=16, top_k=4, I_shared=256),
+     ["router_logits", "router_topk", "permute", "shared_gateup_mfma", "routed_gateup_mfma", "shared_down_mfma",
+      "routed_down_mfma", "combine"]),
+    (variant("mixed", "disp_shared_split", 219, T=16, d=2048, I=128, E=8, top_k=2, I_shared=1024),
+     ["router_logits", "router_topk", "permute", "shared_gateup_mfma", "shared_swiglu", "routed_gateup_mfma",
+      "shared_down_mfma", "shared_sum", "routed_down_mfma", "combine"]),
+    (variant("mixed", "disp_shared_gemv", 218, T=7, d=512, I=256, E=128, top_k=4, I_shared=256),
      ["router_logits", "router_topk", "permute", "shared_gateup", "routed_gateup", "shared_down", "routed_down",
       "combine"]),
-    (variant("mixed", "disp_mixed_mfma", 215, T=64, d=512, I=256, E=16, top_k=4, I_shared=256),
-     ["router_logits", "router_topk", "permute", "shared_gateup", "routed_gateup_mfma", "shared_down",
-      "routed_down_mfma", "combine"]),
     (variant("hash", "disp_hash_gemv", 216, T=40, d=512, I=256, E=64, vocab=1000),
      ["router_hash", "permute", "routed_gateup", "routed_down", "combine"]),
     (variant("prefill", "disp_mxfp4", 217, T=64, d=512, I=256, E=8, top_k=2, bias_kind="normal"),
@@ -160,7 +166,9 @@ def test_deterministic_with_poisoned_workspace():
 def test_dispatch_picks_expected_kernels(cfg, expect):
     """Which kernels a step runs: the fused path for up to 4 top-k tokens; the
     streaming GEMV under one token per expert (2/3-bit) or four (4-bit); the
-    matrix-core grouped GEMM above that."""
+    matrix-core grouped GEMM above that; the shared expert on the matrix cores
+    from 8 tokens, its K split over workgroups (with finishers) while its
+    tiles are few."""
     layer = synth.gen_layer(cfg)
     dl = qm.DeviceLayer.from_host(layer)
     x = xdev(synth.gen_x(cfg, 0))

@@ -50,6 +50,11 @@ SMALL = [
             gate_up=FormatSpec("affine", 3, 64), down=FormatSpec("affine", 2, 128)),
     variant("mixed", "aff4g32_3g32_mixed_paths", 118, T=40, d=512, I=256, E=8, top_k=2, bias_kind="normal",
             gate_up=FormatSpec("affine", 4, 32), down=FormatSpec("affine", 3, 32)),
+    # 8-bit routed experts on the matrix cores (32- and 16-token tiles)
+    variant("mixed", "aff8_mfma", 119, T=64, d=512, I=256, E=8, top_k=4, bias_kind="normal",
+            gate_up=FormatSpec("affine", 8, 128), down=FormatSpec("affine", 8, 32), I_shared=256),
+    # shared expert with its K split over workgroups (4 slices gate/up, 2 down)
+    variant("mixed", "shared_splitk", 120, T=16, d=2048, I=128, E=8, top_k=2, bias_kind="normal", I_shared=1024),
     # 2- and 3-bit codes on the streaming GEMV (under one token per expert)
     variant("mixed", "mixed_gemv", 117, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
 ]
