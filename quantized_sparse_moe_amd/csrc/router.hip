@@ -141,6 +141,62 @@ __global__ __launch_bounds__(256) void k_logits_mfma(const uint16_t* __restrict_
   }
 }
 
+// Mid-size batches (16 < T <= 256): the tile above leaves most of the chip
+// idle (4 x T/16 workgroups), so here a workgroup takes 16 tokens x 16
+// experts and its 16 waves split K (wave w takes K steps w, w + 16, ...). A
+// wave issues the loads of all its steps (up to kLogitsU) before the first
+// MFMA, so one memory round trip covers its share; steps past the end get a
+// zero A fragment. Partial tiles are added in wave order through LDS.
+constexpr int kLogitsWaves = 16;
+constexpr int kLogitsU = 8;
+
+__global__ __launch_bounds__(kLogitsWaves * 64) void k_logits_mfma_ksplit(const uint16_t* __restrict__ x,
+                                                                          const float* __restrict__ wr, int T,
+                                                                          int E, int d,
+                                                                          float* __restrict__ logits) {
+  __shared__ f32x4_t s_part[kLogitsWaves - 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int t0 = blockIdx.y * 16, e0 = blockIdx.x * 16;
+  const uint16_t* xa = x + static_cast<size_t>(min(t0 + r16, T - 1)) * d + 8 * g;
+  const float* wb = wr + static_cast<size_t>(min(e0 + r16, E - 1)) * d + 8 * g;
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nsteps = d / 32;
+  for (int base = wave; base < nsteps; base += kLogitsWaves * kLogitsU) {
+    bf16x8_t af[kLogitsU];
+    u32x4_t bw[kLogitsU][2];
+#pragma unroll
+    for (int u = 0; u < kLogitsU; ++u) {
+      const int k0 = min(base + u * kLogitsWaves, nsteps - 1) * 32;
+      af[u] = *reinterpret_cast<const bf16x8_t*>(xa + k0);
+      bw[u][0] = *reinterpret_cast<const u32x4_t*>(wb + k0);
+      bw[u][1] = *reinterpret_cast<const u32x4_t*>(wb + k0 + 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first MFMA
+#pragma unroll
+    for (int u = 0; u < kLogitsU; ++u) {
+      const bool ok = base + u * kLogitsWaves < nsteps;
+      const bf16x8_t a = ok ? af[u] : bf16x8_t{};
+      bf16x8_t hi, mid, lo;
+      split3_bf16x8(bw[u][0], bw[u][1], hi, mid, lo);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, mid, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc, 0, 0, 0);
+    }
+  }
+  if (wave > 0) s_part[wave - 1][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kLogitsWaves - 1; ++w) acc += s_part[w][lane];
+  const int e = e0 + r16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * g + i;
+    if (t < T && e < E) logits[static_cast<size_t>(t) * E + e] = acc[i];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Top-k: one wave per token (keys staged in LDS, 12 bytes per expert).
 // ---------------------------------------------------------------------------
@@ -255,8 +311,8 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E
     QSMOE_LAUNCH(k_logits_mfma<4>, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, wr, T, E, d,
                        logits);
   } else if (T > 16) {
-    QSMOE_LAUNCH(k_logits_mfma<1>, dim3((E + 63) / 64, (T + 15) / 16), dim3(256), 0, s, x, wr, T, E, d,
-                       logits);
+    QSMOE_LAUNCH(k_logits_mfma_ksplit, dim3((E + 15) / 16, (T + 15) / 16), dim3(kLogitsWaves * 64), 0, s, x, wr,
+                 T, E, d, logits);
   } else if (T == 1) {
     QSMOE_LAUNCH(k_logits_gemv<1>, dim3(E, 1), dim3(256), 0, s, x, wr, T, E, d, logits);
   } else if (T == 2) {

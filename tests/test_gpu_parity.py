@@ -98,11 +98,13 @@ def test_small_layer_parity(cfg):
     print(f"{cfg.name}: max rel err {worst:.2e}")
 
 
-def test_router_logits_and_topk_on_gpu_keys():
+@pytest.mark.parametrize("T,d,E", [(300, 1024, 64), (100, 1056, 40), (17, 4096, 256)])
+def test_router_logits_and_topk_on_gpu_keys(T, d, E):
     """Logits within fp32 accumulation error of float64; the GPU top-k equals
     a host top-k over the GPU's own fp32 logits (scores in fp32), except where
-    two fp32 keys lie within a few ulps."""
-    cfg = variant("prefill", "logits", 111, T=300, d=1024, I=128, E=64)
+    two fp32 keys lie within a few ulps. Shapes: the 64-token tile kernel; the
+    K-split kernel with ragged tokens, experts and K steps; its full width."""
+    cfg = variant("prefill", "logits", 111, T=T, d=d, I=128, E=E)
     wr, bias = synth.gen_router(cfg)
     layer = synth.Layer(cfg, wr, bias, None, synth.gen_routed_stacked(cfg), None)
     dl = qm.DeviceLayer.from_host(layer)
