@@ -376,8 +376,9 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   constexpr int GPS = kKT / G;                       // groups per K step
   constexpr int MB = MT / 16;
   constexpr int ACH = (MT * 16 + 255) / 256;         // 16-byte activation chunks per thread per step
-  __shared__ int32_t s_off[kMaxExperts + 1];
-  __shared__ int32_t s_mt[kMaxExperts + 1];
+  extern __shared__ int32_t s_dyn[];  // expert offsets and m-tile starts, E + 1 each
+  int32_t* const s_off = s_dyn;
+  int32_t* const s_mt = s_dyn + a.E + 1;
   __shared__ int32_t s_src[MT];
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
   // weight macro steps: ROWB bytes of each of a wave's 64 rows
@@ -728,16 +729,17 @@ template <bool GATEUP, int BITS, int MT>
 static void launch_affine(const MfmaArgs& a, hipStream_t s) {
   constexpr int NTILE = (GATEUP ? 32 : 64) * kAffRB;
   const dim3 grid(mfma_grid(a.T, a.k, a.E, a.m0.rows, NTILE, MT, a.ksplit));
+  const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
   if constexpr (MT == 16 && BITS != 3) {
     if (a.m0.group == 32) {
-      QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 32, 16>), grid, dim3(256), 0, s, a);
+      QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 32, 16>), grid, dim3(256), lds, s, a);
       return;
     }
   }
   if (a.m0.group == 64)
-    QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 64, MT>), grid, dim3(256), 0, s, a);
+    QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 64, MT>), grid, dim3(256), lds, s, a);
   else
-    QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 128, MT>), grid, dim3(256), 0, s, a);
+    QSMOE_LAUNCH((k_mfma_affine<GATEUP, BITS, 128, MT>), grid, dim3(256), lds, s, a);
 }
 
 template <bool GATEUP>
