@@ -318,13 +318,14 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 // batches), where the weight stream is the cost. Tiles: MT (16 or 32)
 // bucketed tokens x RB * 16 columns per wave (gate/up: RB/2 blocks of gate
 // and the same rows of up), 4 waves per workgroup. Each wave streams its 64
-// weight rows in macro steps of ROWB bytes per row (128 bytes: 2 K steps of
-// 4-bit codes, 4 of 2-bit; 192 bytes, 4 K steps, for 3-bit): every load
-// instruction covers whole rows of the macro step (8 rows x 128 bytes, or
-// 4 x 192), so it touches each cache line once; reading 16 rows x 32 bytes
-// per instruction instead measured 25 % less bandwidth from the same
-// number of bytes. The macro step is staged in registers one macro step
-// ahead and written to the wave's own padded LDS slot, from which lane
+// weight rows in macro steps of ROWB bytes per row (128 bytes: 1 K step of
+// 8-bit codes, 2 of 4-bit, 4 of 2-bit; 96 bytes, 2 K steps, of 3-bit, which
+// keeps that format's staging registers and LDS slot small): every load
+// instruction covers 8 rows of the macro step, so it touches few cache
+// lines; reading 16 rows x 32 bytes per instruction instead measured 25 %
+// less bandwidth from the same number of bytes. The macro step is staged
+// in registers one macro step ahead and written to the wave's own padded
+// LDS slot, from which lane
 // group g of pass s reads the 8-code chunk of inputs 32 s + 8 g .. + 7 and
 // recasts it as one word (code i at bit b i, code i + 4 at bit 16 + b i).
 // Scales and biases are fetched once per 4 K steps (lane group q holds step
@@ -365,10 +366,16 @@ __device__ __forceinline__ bf16x8_t chunk_to_bf16x8(const uint32_t (&f)[BITS == 
 }
 
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
+#ifndef QSMOE_AFF_UNROLL
+#define QSMOE_AFF_UNROLL 8
+#endif
+#ifndef QSMOE_AFF_MINWG
+#define QSMOE_AFF_MINWG 2
+#endif
 
 
 template <bool GATEUP, int BITS, int G, int MT>
-__global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
+__global__ __launch_bounds__(256, QSMOE_AFF_MINWG) void k_mfma_affine(MfmaArgs a) {
   constexpr int RB = kAffRB;
   constexpr int HB = GATEUP ? RB / 2 : RB;           // row blocks per matrix per wave
   constexpr int NTILE = 4 * HB * 16;                 // rows per matrix per workgroup
@@ -384,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   // weight macro steps: ROWB bytes of each of a wave's 64 rows
   constexpr int QW = BITS == 8 ? 2 : 1;         // words per 8-code chunk as read
   constexpr float kOff = BITS == 8 ? 0.0f : 128.0f;  // value of code 0 as decoded
-  constexpr int LPR = BITS == 3 ? 16 : 8;       // lanes per row in one load
+  constexpr int LPR = 8;                        // lanes per row in one load
   constexpr int BPL = BITS == 3 ? 12 : 16;      // bytes per lane in one load
   constexpr int ROWB = LPR * BPL;               // bytes per row per macro step
   constexpr int SPM = ROWB * 8 / (BITS * kKT);  // K steps per macro step
@@ -392,7 +399,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
   constexpr int NIM = 64 / RPI;                 // loads per macro step
   constexpr int LSTR = ROWB + 16;               // LDS bytes per row (padded against bank conflicts)
   constexpr int BW = BPL / 4;
-  static_assert(8 % SPM == 0 && RB * 16 == 64, "macro steps tile the 8-step unrolled rounds and 64 rows");
+  static_assert(4 % SPM == 0 && RB * 16 == 64, "macro steps tile the unrolled rounds and 64 rows");
   __shared__ __attribute__((aligned(16))) uint32_t s_b[4][64 * LSTR / 4];  // per wave
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -647,6 +654,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
     load_a(a_reg0, min(ks_begin + 1, nsteps - 1) * kKT);
     lds_barrier();
     int ks = ks_begin;
+#if QSMOE_AFF_UNROLL == 8
     for (; ks + 8 <= ks_end; ks += 8) {
       step(ks, J0{}, a_reg1, a_reg0);
       step(ks + 1, J1{}, a_reg0, a_reg1);
@@ -664,6 +672,17 @@ __global__ __launch_bounds__(256, 2) void k_mfma_affine(MfmaArgs a) {
     if (ks + 4 < ks_end) step(ks + 4, J4{}, a_reg1, a_reg0);
     if (ks + 5 < ks_end) step(ks + 5, J5{}, a_reg0, a_reg1);
     if (ks + 6 < ks_end) step(ks + 6, J6{}, a_reg1, a_reg0);
+#else
+    for (; ks + 4 <= ks_end; ks += 4) {
+      step(ks, J0{}, a_reg1, a_reg0);
+      step(ks + 1, J1{}, a_reg0, a_reg1);
+      step(ks + 2, J2{}, a_reg1, a_reg0);
+      step(ks + 3, J3{}, a_reg0, a_reg1);
+    }
+    if (ks < ks_end) step(ks, J0{}, a_reg1, a_reg0);
+    if (ks + 1 < ks_end) step(ks + 1, J1{}, a_reg0, a_reg1);
+    if (ks + 2 < ks_end) step(ks + 2, J2{}, a_reg1, a_reg0);
+#endif
   };
   if constexpr (MB == 2) {
     if (valid_mb == 2)
