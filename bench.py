@@ -78,10 +78,15 @@ def kernel_bytes(name, cfg, dl, T, touched):
         return touched * (r.gate.nbytes_per_expert() + r.up.nbytes_per_expert()) + T * d * 2 + tk * I * 2
     if name in ("routed_down", "routed_down_mfma"):
         return touched * r.down.nbytes_per_expert() + tk * I * 2 + tk * d * 4
-    if name == "shared_gateup":
+    if name in ("shared_gateup", "shared_gateup_mfma"):
         return sh.gate.nbytes_per_expert() + sh.up.nbytes_per_expert() + T * d * 2 + T * cfg.I_shared * 2
-    if name == "shared_down":
+    if name in ("shared_down", "shared_down_mfma"):
         return sh.down.nbytes_per_expert() + T * cfg.I_shared * 2 + T * d * 4
+    # finishers of a K-split shared expert: one slice of fp32 partials in, the result out
+    if name == "shared_swiglu":
+        return T * cfg.I_shared * (2 * 4 + 2)
+    if name == "shared_sum":
+        return T * d * (4 + 4)
     if name == "combine":
         return tk * d * 4 + tk * 4 + (T * d * 4 if sh is not None else 0) + T * d * 2
     # fused small-batch path
@@ -105,6 +110,10 @@ def kernel_flops(name, cfg, T):
         return 2.0 * tk * cfg.d * 2 * cfg.I
     if name == "routed_down_mfma":
         return 2.0 * tk * cfg.I * cfg.d
+    if name == "shared_gateup_mfma":
+        return 2.0 * T * cfg.d * 2 * cfg.I_shared
+    if name == "shared_down_mfma":
+        return 2.0 * T * cfg.I_shared * cfg.d
     return None
 
 

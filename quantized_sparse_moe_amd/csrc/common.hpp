@@ -79,6 +79,7 @@ __device__ __forceinline__ float xchg(float v, int mask) {
 // reduce_multi_index<N>(lane).
 template <int N>
 __device__ __forceinline__ float wave_reduce_multi(const float (&v)[N]) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "the halving exchange needs a power-of-two count");
   float cur[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) cur[i] = v[i];

@@ -146,6 +146,8 @@ def test_deterministic_with_poisoned_workspace():
 @pytest.mark.parametrize("cfg,expect", [
     (variant("decode", "disp_dec", 213, T=2, d=512, I=256, E=32, I_shared=256),
      ["dec_router", "dec_gateup", "dec_down_combine"]),
+    (variant("decode", "disp_dec1", 220, T=1, d=512, I=256, E=32, I_shared=256),
+     ["dec_router", "dec_gateup", "dec_down_combine"]),
     (variant("mixed", "disp_mixed_gemv", 214, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
      ["router_logits", "router_topk", "permute", "shared_gateup_mfma", "routed_gateup", "shared_down_mfma",
       "routed_down", "combine"]),

@@ -55,6 +55,10 @@ SMALL = [
             gate_up=FormatSpec("affine", 8, 128), down=FormatSpec("affine", 8, 32), I_shared=256),
     # shared expert with its K split over workgroups (4 slices gate/up, 2 down)
     variant("mixed", "shared_splitk", 120, T=16, d=2048, I=128, E=8, top_k=2, bias_kind="normal", I_shared=1024),
+    # single token on the fused path: k of 6 (shared expert), 2 (hidden 4096, none), 8 (40 experts)
+    variant("decode", "fused_k6_shared", 121, T=1, d=1024, I=256, E=64, top_k=6, I_shared=256),
+    variant("decode", "fused_k2_d4096", 122, T=1, d=4096, I=128, E=16, top_k=2, shared=None),
+    variant("decode", "fused_k8_e40", 123, T=1, d=512, I=384, E=40, top_k=8, I_shared=128),
     # 2- and 3-bit codes on the streaming GEMV (under one token per expert)
     variant("mixed", "mixed_gemv", 117, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
 ]
