@@ -125,6 +125,94 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   QSMOE_TL(1, 7);
 }
 
+// Launch 2 for a single token: one 512-thread workgroup per CU takes an equal
+// share of the (slot, row) units, and inside it the 8 waves take rows one at
+// a time from an LDS counter, the next row's loads issued before the current
+// row is computed. Two waves share each SIMD and the older one is issued
+// first: with a fixed split per wave (or per workgroup, two per CU) the
+// younger half measured ~20 % slower and the launch ended with it.
+template <int F, int B, int CPL>
+__global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
+  __shared__ int32_t s_ids[kDecMaxK];
+  __shared__ uint32_t s_next;
+  QSMOE_TL(1, 0);
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    uint64_t key[4];
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      const bool ok = e < a.E;
+      key[i] = a.keys[ok ? e : 0];
+      sc[i] = a.scores[ok ? e : 0];
+      key[i] = ok ? key[i] : 0;
+    }
+    int id;
+    float wt;
+    topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
+    if (lane < a.k) {
+      s_ids[lane] = id;
+      if (blockIdx.x == 0) {
+        a.ids[lane] = id;
+        a.w[lane] = wt;
+      }
+    }
+  }
+  const int rows = a.gate.rows, nchunks = a.gate.cols >> 5;
+  const uint32_t total = static_cast<uint32_t>(a.k) * rows;
+  const uint32_t u_begin = static_cast<uint32_t>(static_cast<uint64_t>(total) * blockIdx.x / gridDim.x);
+  const uint32_t u_end = static_cast<uint32_t>(static_cast<uint64_t>(total) * (blockIdx.x + 1) / gridDim.x);
+  if (threadIdx.x == 0) s_next = u_begin;
+  const uint16_t* xrow[1] = {a.x};
+  const bool xvalid[1] = {true};
+  XRaw<CPL, 1> xw;
+  load_x_raw<CPL, 1>(xw, xrow, lane, nchunks);
+  __syncthreads();
+  QSMOE_TL(1, 1);
+  if (u_begin >= u_end) return;
+  auto grab = [&]() -> uint32_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&s_next, 1u);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  using Batch = RowBatch<F, B, CPL, true, 1>;
+  // loads are unconditional: a unit past the end reloads the last one
+  auto load_unit = [&](Batch& b, uint32_t u) {
+    const uint32_t uc = min(u, u_end - 1);
+    const int slot = static_cast<int>(uc / rows), r = static_cast<int>(uc - static_cast<uint32_t>(slot) * rows);
+    const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
+    load_batch<F, B, CPL, true, 1>(b, expert_slice(a.gate, e), expert_slice(a.up, e), r, r + 1, lane, nchunks);
+  };
+  XRegs<F, B, CPL, 1> xr;
+  auto compute_unit = [&](const Batch& b, uint32_t u) {
+    const int slot = static_cast<int>(u / rows), r = static_cast<int>(u - static_cast<uint32_t>(slot) * rows);
+    uint16_t* hs = a.h + static_cast<size_t>(slot) * rows;
+    auto store = [&](int, int rr, float g, float up) {
+      hs[rr] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * up));
+    };
+    compute_batch<F, B, CPL, 1, true, 1>(b, xr, r, r + 1, lane, nchunks, store);
+  };
+  Batch A, Bb;
+  uint32_t u0 = grab();
+  load_unit(A, u0);
+  finish_x<F, B, CPL, 1>(xr, xw, xvalid, lane, nchunks);
+  if (u0 < u_end) {
+    while (true) {
+      const uint32_t u1 = grab();
+      load_unit(Bb, u1);
+      compute_unit(A, u0);
+      if (u1 >= u_end) break;
+      const uint32_t u2 = grab();
+      load_unit(A, u2);
+      compute_unit(Bb, u1);
+      if (u2 >= u_end) break;
+      u0 = u2;
+    }
+  }
+  QSMOE_TL(1, 7);
+}
+
 // ---------------------------------------------------------------------------
 // Partial (this lane's) dot of one row with token j's activations.
 template <int F, int B, int CPL, int NT>
@@ -366,8 +454,32 @@ hipError_t launch_dec_router(const DecodeArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return n;
+}
+
+#ifndef QSMOE_DEC_GU1
+#define QSMOE_DEC_GU1 1
+#endif
+
 hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
   const int cpl = dec_cpl(a.gate.cols);
+  const int cus = device_cus();
+  if (QSMOE_DEC_GU1 && a.T == 1 && cus > 0 && cpl <= 2) {  // (hidden > 4096 would spill at 512 threads)
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(cus, static_cast<int64_t>(a.k) * a.gate.rows))), block(512);
+    QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
+      if (cpl == 1)
+        QSMOE_LAUNCH((k_dec_gateup1<F, B, 1>), grid, block, 0, s, a);
+      else
+        QSMOE_LAUNCH((k_dec_gateup1<F, B, 2>), grid, block, 0, s, a);
+    })
+    return hipGetLastError();
+  }
   const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.k * a.gate.rows, QSMOE_DEC_GU_MIN_ROWS)), block(256);
   QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
     if (cpl == 1)
