@@ -38,6 +38,12 @@ hipError_t timeline_copy(void* host, size_t bytes) {
 }
 #endif
 
+// Single-token launch 2 with one 512-thread workgroup per CU.
+#ifndef QSMOE_DEC_GU1
+#define QSMOE_DEC_GU1 1
+#endif
+
+
 constexpr int kDecMaxT = 4;
 constexpr int kDecMaxK = 8;
 
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
     const bool xvalid[1] = {true};
     XRaw<CPL, 1> xw;
     load_x_raw<CPL, 1>(xw, xrow, lane, nchunks);
-    const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
+    const int e = min(max(__builtin_amdgcn_readfirstlane(s_ids[slot]), 0), a.E - 1);
     const QMat q0 = expert_slice(a.gate, e), q1 = expert_slice(a.up, e);
     uint16_t* hs = a.h + static_cast<size_t>(slot) * rows;
     stream_rows<F, B, CPL, 1, true, 1>(q0, q1, xw, xvalid, r_begin, r_end, lane, nchunks,
@@ -181,7 +187,7 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   auto load_unit = [&](Batch& b, uint32_t u) {
     const uint32_t uc = min(u, u_end - 1);
     const int slot = static_cast<int>(uc / rows), r = static_cast<int>(uc - static_cast<uint32_t>(slot) * rows);
-    const int e = __builtin_amdgcn_readfirstlane(s_ids[slot]);
+    const int e = min(max(__builtin_amdgcn_readfirstlane(s_ids[slot]), 0), a.E - 1);
     load_batch<F, B, CPL, true, 1>(b, expert_slice(a.gate, e), expert_slice(a.up, e), r, r + 1, lane, nchunks);
   };
   XRegs<F, B, CPL, 1> xr;
@@ -462,10 +468,6 @@ static int device_cus() {
   }
   return n;
 }
-
-#ifndef QSMOE_DEC_GU1
-#define QSMOE_DEC_GU1 1
-#endif
 
 hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
   const int cpl = dec_cpl(a.gate.cols);
