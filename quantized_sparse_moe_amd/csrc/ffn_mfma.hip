@@ -301,6 +301,202 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   }
 }
 
+#ifndef MXW_WN
+#define MXW_WN 4  // waves along the output rows (4: each wave takes all 128 tokens)
+#endif
+#define MXW_MT (4 / (4 / MXW_WN))
+
+// ---------------------------------------------------------------------------
+// MXFP4 grouped GEMM on 32 x 32 tiles (V_MFMA_F32_32X32X16_BF16).
+//
+// Workgroup: 128 bucketed tokens x 128 output columns: 128 rows of gate and
+// the same 128 rows of up, or 256 rows of down. Its 4 waves split the
+// columns; each takes all 128 tokens x 64 columns (gate/up: 32 rows of gate
+// + the same 32 of up, so the SwiGLU pairs meet in one lane) as 4 x 2
+// accumulator tiles of 32 x 32. (A 2 x 2 grid of waves, each 64 tokens x
+// 64 columns, loads and converts every weight twice and measured slower.)
+// Operand layouts (checked on the device): A lane l holds row
+// l % 32, inputs 8 (l / 32) .. + 7 of the pass; B lane l holds column l % 32
+// and the same inputs; element i of D in lane l is row
+// 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32. In a 128-input K step lane
+// group g = l / 32 holds inputs 64 g .. 64 g + 63, pass p (0..7) using inputs
+// 64 g + 8 p .. + 7 for A and B alike (the sum does not care which pass adds
+// which input), so a lane's weights for the whole step are 32 contiguous
+// bytes of its row (two 16-byte loads) with the two e8m0 exponents that
+// cover them. Per pass a wave reads 4 activation fragments from LDS and
+// converts 2 weight fragments for 8 MFMAs of 32 x 32 x 16. Activations are
+// staged as in k_mfma_mxfp4.
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
+  typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+  constexpr int MT = 128;
+  constexpr int MTW = MXW_MT;                // 32-token tiles per wave
+  constexpr int WM = 4 / MXW_WN;             // waves along the tokens
+  constexpr int NTILE = (GATEUP ? 32 : 64) * MXW_WN;  // output rows per workgroup (per matrix)
+  static_assert(WM * MTW * 32 == 128, "the waves along M cover the 128-token tile");
+  constexpr int ACH = MT * 16 / 256;        // 16-byte activation chunks per thread per K step
+  extern __shared__ int32_t s_dyn[];        // expert offsets and m-tile starts, E + 1 each
+  int32_t* const s_off = s_dyn;
+  int32_t* const s_mt = s_dyn + a.E + 1;
+  __shared__ int32_t s_src[MT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int wm = wave % WM, wn = wave / WM;
+  const int n = a.T * a.k;
+  const int rows = a.m0.rows, cols = a.m0.cols;
+  Tile t;
+  if (!tile_of_block<MT>(a, rows / NTILE, s_off, s_mt, t)) return;
+  const int e = __builtin_amdgcn_readfirstlane(t.e), p0 = __builtin_amdgcn_readfirstlane(t.p0);
+  const int count = __builtin_amdgcn_readfirstlane(t.count), ntile = __builtin_amdgcn_readfirstlane(t.ntile);
+  if (tid < MT) {
+    const int p = p0 + min(tid, count - 1);
+    s_src[tid] = GATEUP && !a.shared ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
+  }
+  __syncthreads();
+
+  // activations: in round i thread t copies 16 bytes, chunk t % 16 of token
+  // row t / 16 + 16 i (rows past the tile's tokens repeat its last token)
+  const int a_chunk = tid & 15, a_row0 = tid >> 4;
+  uint32_t a_off[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) a_off[i] = static_cast<uint32_t>(s_src[a_row0 + 16 * i]) * cols + a_chunk * 8;
+  auto load_a = [&](u32x4_t (&ar)[ACH], int k0) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) ar[i] = *reinterpret_cast<const u32x4_t*>(a.x + a_off[i] + k0);
+  };
+  auto store_a = [&](const u32x4_t (&ar)[ACH], int buf) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row0 + 16 * i][a_chunk * 8]) = ar[i];
+  };
+
+  // weights: block 0 = rows row0 of gate (or down), block 1 = the same rows
+  // of up (or rows row0 + 32 of down)
+  const QMat w0 = expert_slice(a.m0, e);
+  const QMat w1 = expert_slice(a.m1, e);
+  const int g = lane >> 5, r32 = lane & 31;
+  const int row0 = ntile * NTILE + wn * (GATEUP ? 32 : 64) + r32;
+  const size_t rb_bytes = static_cast<size_t>(w0.row_words) * 4, rg = static_cast<size_t>(w0.row_groups);
+  const uint8_t* cb[2];
+  const uint8_t* sb[2];
+  cb[0] = reinterpret_cast<const uint8_t*>(w0.codes) + static_cast<size_t>(row0) * rb_bytes + 32 * g;
+  sb[0] = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(row0) * rg + 2 * g;
+  if constexpr (GATEUP) {
+    cb[1] = reinterpret_cast<const uint8_t*>(w1.codes) + static_cast<size_t>(row0) * rb_bytes + 32 * g;
+    sb[1] = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(row0) * rg + 2 * g;
+  } else {
+    cb[1] = cb[0] + 32 * rb_bytes;
+    sb[1] = sb[0] + 32 * rg;
+  }
+  struct BRegs {
+    u32x4_t c[2][2];  // [block][half]: 32 bytes = 64 codes
+    uint32_t s[2];    // [block]: the two e8m0 bytes of the step (groups 2g, 2g + 1)
+  };
+  auto load_b = [&](BRegs& b, int k0) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const uint8_t* cp = cb[blk] + k0 / 2;
+      b.c[blk][0] = *reinterpret_cast<const u32x4_t*>(cp);
+      b.c[blk][1] = *reinterpret_cast<const u32x4_t*>(cp + 16);
+      b.s[blk] = *reinterpret_cast<const uint16_t*>(sb[blk] + k0 / 32);
+    }
+  };
+
+  f32x16_t acc[MTW][2];
+#pragma unroll
+  for (int i = 0; i < MTW; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int nmt = min(MTW, max(0, (count - 32 * MTW * wm + 31) / 32));  // this wave's 32-token tiles with tokens
+  const int nsteps = cols / kKT;
+  // activations and weights one K step ahead (a step is ~2000 MFMA cycles
+  // per wave); weights in a register ring. (Staging the activations in two
+  // halves, to free registers, measured 4 % slower: the second half then
+  // has only half a step to arrive.)
+  u32x4_t a_reg[ACH];
+  BRegs b_reg0, b_reg1;
+  auto kloop = [&](auto nmt_tag) {
+    constexpr int NMT = decltype(nmt_tag)::value;
+    auto step = [&](int ks, const BRegs& b_use, BRegs& b_ld) {
+      const int buf = ks & 1;
+      const int kn = min(ks + 1, nsteps - 1) * kKT;
+      load_a(a_reg, kn);
+      load_b(b_ld, kn);
+      if constexpr (NMT > 0) {
+        float sc[2][2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          sc[blk][0] = e8m0_to_f32(b_use.s[blk] & 0xffu);
+          sc[blk][1] = e8m0_to_f32((b_use.s[blk] >> 8) & 0xffu);
+        }
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          bf16x8_t af[NMT];
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt)
+            af[mt] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][32 * MTW * wm + 32 * mt + r32][64 * g + 8 * p]);
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const bf16x8_t bf = fp4_to_bf16x8(b_use.c[blk][p >> 2][p & 3], sc[blk][p >> 2]);
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt)
+              acc[mt][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf, acc[mt][blk], 0, 0, 0);
+          }
+        }
+      }
+      store_a(a_reg, buf ^ 1);  // after the last step: unused, harmless
+      lds_barrier();
+    };
+    load_b(b_reg0, 0);
+    load_a(a_reg, 0);
+    store_a(a_reg, 0);
+    lds_barrier();
+    int ks = 0;
+    for (; ks + 2 <= nsteps; ks += 2) {
+      step(ks, b_reg0, b_reg1);
+      step(ks + 1, b_reg1, b_reg0);
+    }
+    if (ks < nsteps) step(ks, b_reg0, b_reg1);
+  };
+  if constexpr (MTW == 4) {
+    switch (nmt) {
+      case 4: kloop(std::integral_constant<int, 4>{}); break;
+      case 3: kloop(std::integral_constant<int, 3>{}); break;
+      case 2: kloop(std::integral_constant<int, 2>{}); break;
+      case 1: kloop(std::integral_constant<int, 1>{}); break;
+      default: kloop(std::integral_constant<int, 0>{}); break;
+    }
+  } else {
+    if (nmt == 2)
+      kloop(std::integral_constant<int, 2>{});
+    else if (nmt == 1)
+      kloop(std::integral_constant<int, 1>{});
+    else
+      kloop(std::integral_constant<int, 0>{});
+  }
+
+  // epilogue: element i of lane l is token 32 MTW wm + 32 mt + 8 (i / 4) + 4 g + i % 4
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt) {
+    if (mt >= nmt) continue;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int tl = 32 * MTW * wm + 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (tl >= count) continue;
+      if constexpr (GATEUP) {
+        a.h[static_cast<size_t>(p0 + tl) * rows + row0] =
+            static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mt][0][i]) * acc[mt][1][i]));
+      } else {
+        const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
+        float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
+        yrow[0] = acc[mt][0][i];
+        yrow[32] = acc[mt][1][i];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Affine b-bit experts, b in {2, 3, 4} (w = s q + b per group of G inputs,
 // fp16 s and b).
@@ -366,6 +562,9 @@ __device__ __forceinline__ bf16x8_t chunk_to_bf16x8(const uint32_t (&f)[BITS == 
 }
 
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
+#ifndef QSMOE_MXFP4_W
+#define QSMOE_MXFP4_W 1
+#endif
 #ifndef QSMOE_AFF_UNROLL
 #define QSMOE_AFF_UNROLL 8
 #endif
@@ -764,7 +963,11 @@ static void launch_affine(const MfmaArgs& a, hipStream_t s) {
 template <bool GATEUP>
 static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   const QMat& m = a.m0;
-  if (m.fmt == 1) {
+  if (m.fmt == 1 && QSMOE_MXFP4_W && m.rows % ((GATEUP ? 32 : 64) * MXW_WN) == 0) {
+    const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
+    QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP>),
+                 dim3(mfma_grid(a.T, a.k, a.E, m.rows, (GATEUP ? 32 : 64) * MXW_WN, 128)), dim3(256), lds, s, a);
+  } else if (m.fmt == 1) {
     // measured: gate/up best with 128-token tiles x 32 columns per wave, down
     // with 64-token tiles x 64 columns per wave
     constexpr int MT = GATEUP ? 128 : 64, RB = GATEUP ? 2 : 4;

@@ -36,6 +36,10 @@ SMALL = [
     # matrix-core paths: MXFP4 buckets spanning two 128-token tiles; affine
     # 4-bit buckets spanning several 32-token tiles, groups of 32, 64 and 128
     variant("prefill", "mxfp4_big_bucket", 112, T=300, d=256, I=128, E=4, top_k=2, bias_kind="normal"),
+    # MXFP4 output widths off the 32 x 32 kernel's 128-column tile: gate/up of
+    # 320 rows, down of 384 rows take the 16 x 16 kernel
+    variant("prefill", "mxfp4_gateup_16x16", 124, T=150, d=256, I=320, E=4, top_k=2, bias_kind="normal"),
+    variant("prefill", "mxfp4_down_16x16", 125, T=150, d=384, I=256, E=4, top_k=2, bias_kind="normal"),
     variant("prefill", "aff4_g32_g128_mfma", 113, T=96, d=512, I=256, E=8, top_k=2, bias_kind="normal",
             gate_up=FormatSpec("affine", 4, 32), down=FormatSpec("affine", 4, 128)),
     variant("prefill", "aff4_g64_mfma_shared", 114, T=80, d=768, I=384, E=16, top_k=4, bias_kind="normal",
