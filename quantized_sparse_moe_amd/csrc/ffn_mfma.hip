@@ -59,6 +59,20 @@ struct MfmaArgs {
   float* part;             // [ksplit][T*k][2 I] (gate/up: g then u) or [ksplit][T*k][d]
 };
 
+typedef __attribute__((address_space(1))) void global_void_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// direct global -> LDS load of 16 bytes per lane (gfx950's
+// GLOBAL_LOAD_LDS_DWORDX4): lane l's bytes land at lds + 16 l; lds must be
+// the same for the whole wave. Counted by vmcnt, like any vector load.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds((global_void_t*)(src), (lds_void_t*)(lds), 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(0), leaving the LDS/scalar and export counters alone
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+__device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 __device__ __forceinline__ bf16x8_t fp4_to_bf16x8(uint32_t word, float scale) {
   uint32_t r[4];
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0));
@@ -305,11 +319,17 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 #define MXW_WN 4  // waves along the output rows (4: each wave takes all 128 tokens)
 #endif
 #define MXW_MT (4 / (4 / MXW_WN))
+#ifndef QSMOE_MXW_PIN_LOADS
+#define QSMOE_MXW_PIN_LOADS 1
+#endif
+#ifndef QSMOE_MXFP4_SCS
+#define QSMOE_MXFP4_SCS 2  // K steps per scale load in k_mfma_mxfp4_w (1, 2 or 4)
+#endif
 
 // ---------------------------------------------------------------------------
 // MXFP4 grouped GEMM on 32 x 32 tiles (V_MFMA_F32_32X32X16_BF16).
 //
-// Workgroup: 128 bucketed tokens x 128 output columns: 128 rows of gate and
+// Workgroup: 128 bucketed tokens x 256 output columns: 128 rows of gate and
 // the same 128 rows of up, or 256 rows of down. Its 4 waves split the
 // columns; each takes all 128 tokens x 64 columns (gate/up: 32 rows of gate
 // + the same 32 of up, so the SwiGLU pairs meet in one lane) as 4 x 2
@@ -324,9 +344,8 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 // which input), so a lane's weights for the whole step are 32 contiguous
 // bytes of its row (two 16-byte loads) with the two e8m0 exponents that
 // cover them. Per pass a wave reads 4 activation fragments from LDS and
-// converts 2 weight fragments for 8 MFMAs of 32 x 32 x 16. Activations are
-// staged as in k_mfma_mxfp4.
-template <bool GATEUP>
+// converts 2 weight fragments for 8 MFMAs of 32 x 32 x 16.
+template <bool GATEUP, int SCS>
 __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
   typedef __attribute__((ext_vector_type(16))) float f32x16_t;
   constexpr int MT = 128;
@@ -339,9 +358,13 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
   int32_t* const s_off = s_dyn;
   int32_t* const s_mt = s_dyn + a.E + 1;
   __shared__ int32_t s_src[MT];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
+  // the two activation buffers are separate objects, so the compiler can
+  // tell reads of one from the direct-to-LDS loads into the other
+  __shared__ __attribute__((aligned(16))) uint16_t s_a0[MT * kKT];
+  __shared__ __attribute__((aligned(16))) uint16_t s_a1[MT * kKT];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
   const int wm = wave % WM, wn = wave / WM;
   const int n = a.T * a.k;
   const int rows = a.m0.rows, cols = a.m0.cols;
@@ -355,42 +378,47 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
   }
   __syncthreads();
 
-  // activations: in round i thread t copies 16 bytes, chunk t % 16 of token
-  // row t / 16 + 16 i (rows past the tile's tokens repeat its last token)
-  const int a_chunk = tid & 15, a_row0 = tid >> 4;
+  // activations: direct global -> LDS loads, 16 bytes per lane. Round i of
+  // wave w fills the 1 KB of tile rows 4 b .. 4 b + 3, b = 8 w + i: lane l
+  // writes slot l % 16 of row 4 b + l / 16 (rows of 256 bytes, unpadded), and
+  // slot s of row r holds input chunk s ^ (r % 16) of the step, so the 16
+  // rows that 16 lanes read at once hold a chunk in 16 different slots (no
+  // bank conflicts). Rows past the tile's tokens repeat its last token.
   uint32_t a_off[ACH];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) a_off[i] = static_cast<uint32_t>(s_src[a_row0 + 16 * i]) * cols + a_chunk * 8;
-  auto load_a = [&](u32x4_t (&ar)[ACH], int k0) {
+  for (int i = 0; i < ACH; ++i) {
+    const int row = 4 * (ACH * wave + i) + (lane >> 4), slot = lane & 15;
+    a_off[i] = static_cast<uint32_t>(s_src[row]) * cols + 8 * (slot ^ (row & 15));
+  }
+  auto load_a = [&](uint16_t* buf, int k0) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) ar[i] = *reinterpret_cast<const u32x4_t*>(a.x + a_off[i] + k0);
+    for (int i = 0; i < ACH; ++i)
+      load_lds16(a.x + a_off[i] + k0, buf + (ACH * wave + i) * 512);
   };
-  auto store_a = [&](const u32x4_t (&ar)[ACH], int buf) {
-#pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row0 + 16 * i][a_chunk * 8]) = ar[i];
-  };
+  // fragment reads: lane (r32, g) takes chunk 8 g + p of its row in pass p
+  const int xr = r32 & 15;
+  const int a_rd = r32 * kKT + 8 * ((8 * g) ^ (xr & 8));
 
   // weights: block 0 = rows row0 of gate (or down), block 1 = the same rows
   // of up (or rows row0 + 32 of down)
   const QMat w0 = expert_slice(a.m0, e);
   const QMat w1 = expert_slice(a.m1, e);
-  const int g = lane >> 5, r32 = lane & 31;
   const int row0 = ntile * NTILE + wn * (GATEUP ? 32 : 64) + r32;
   const size_t rb_bytes = static_cast<size_t>(w0.row_words) * 4, rg = static_cast<size_t>(w0.row_groups);
   const uint8_t* cb[2];
-  const uint8_t* sb[2];
+  const uint8_t* sb[2];  // the row's e8m0 bytes
   cb[0] = reinterpret_cast<const uint8_t*>(w0.codes) + static_cast<size_t>(row0) * rb_bytes + 32 * g;
-  sb[0] = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(row0) * rg + 2 * g;
+  sb[0] = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(row0) * rg;
   if constexpr (GATEUP) {
     cb[1] = reinterpret_cast<const uint8_t*>(w1.codes) + static_cast<size_t>(row0) * rb_bytes + 32 * g;
-    sb[1] = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(row0) * rg + 2 * g;
+    sb[1] = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(row0) * rg;
   } else {
     cb[1] = cb[0] + 32 * rb_bytes;
     sb[1] = sb[0] + 32 * rg;
   }
   struct BRegs {
     u32x4_t c[2][2];  // [block][half]: 32 bytes = 64 codes
-    uint32_t s[2];    // [block]: the two e8m0 bytes of the step (groups 2g, 2g + 1)
+    uint32_t s[2];    // [block]: the two e8m0 bytes of the step (groups 2g, 2g + 1), SCS == 1
   };
   auto load_b = [&](BRegs& b, int k0) {
 #pragma unroll
@@ -398,8 +426,18 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
       const uint8_t* cp = cb[blk] + k0 / 2;
       b.c[blk][0] = *reinterpret_cast<const u32x4_t*>(cp);
       b.c[blk][1] = *reinterpret_cast<const u32x4_t*>(cp + 16);
-      b.s[blk] = *reinterpret_cast<const uint16_t*>(sb[blk] + k0 / 32);
+      if constexpr (SCS == 1) b.s[blk] = *reinterpret_cast<const uint16_t*>(sb[blk] + k0 / 32 + 2 * g);
     }
+  };
+  // SCS > 1: the e8m0 bytes of SCS K steps in one 4 SCS-byte load per
+  // block (byte 4 j + 2 g + h = group 2 g + h of step j), issued one step
+  // before the first of them is needed. A 2-byte load per lane and step
+  // costs about as much as a 16-byte one: each touches 32 rows' cache lines.
+  typedef __attribute__((ext_vector_type(SCS == 1 ? 1 : SCS))) uint32_t scv_t;
+  scv_t scn[2];
+  auto load_sn = [&](int k0) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) scn[blk] = *reinterpret_cast<const scv_t*>(sb[blk] + k0 / 32);
   };
 
   f32x16_t acc[MTW][2];
@@ -411,31 +449,50 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
   const int nmt = min(MTW, max(0, (count - 32 * MTW * wm + 31) / 32));  // this wave's 32-token tiles with tokens
   const int nsteps = cols / kKT;
   // activations and weights one K step ahead (a step is ~2000 MFMA cycles
-  // per wave); weights in a register ring. (Staging the activations in two
-  // halves, to free registers, measured 4 % slower: the second half then
-  // has only half a step to arrive.)
-  u32x4_t a_reg[ACH];
+  // per wave); weights in a register ring
   BRegs b_reg0, b_reg1;
   auto kloop = [&](auto nmt_tag) {
     constexpr int NMT = decltype(nmt_tag)::value;
-    auto step = [&](int ks, const BRegs& b_use, BRegs& b_ld) {
-      const int buf = ks & 1;
+    // J: the step's place in its group of 4 (its parity picks the buffers;
+    // J % SCS is its place in its scale chunk)
+    auto step = [&](auto j_tag, int ks, const BRegs& b_use, BRegs& b_ld) {
+      constexpr int J = decltype(j_tag)::value;
+      uint16_t* const rd = (J & 1) ? s_a1 : s_a0;
+      uint16_t* const wr = (J & 1) ? s_a0 : s_a1;
       const int kn = min(ks + 1, nsteps - 1) * kKT;
-      load_a(a_reg, kn);
+      uint32_t sw[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        if constexpr (SCS == 1)
+          sw[blk] = b_use.s[blk];
+        else
+          sw[blk] = scn[blk][J % SCS] >> (16 * g);
+      }
+      load_a(wr, kn);  // after the last step: unused, harmless
       load_b(b_ld, kn);
+      if constexpr (SCS > 1 && J % SCS == SCS - 1) {
+        if (ks + 1 < nsteps) load_sn(kn);
+      }
+#if QSMOE_MXW_PIN_LOADS
+      // keep the next step's loads at the top of this one: left to itself the
+      // scheduler sinks them behind most of the MFMAs, and the wait before
+      // the barrier then exposes their latency
+      __builtin_amdgcn_sched_barrier(0);
+#endif
       if constexpr (NMT > 0) {
         float sc[2][2];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-          sc[blk][0] = e8m0_to_f32(b_use.s[blk] & 0xffu);
-          sc[blk][1] = e8m0_to_f32((b_use.s[blk] >> 8) & 0xffu);
+          sc[blk][0] = e8m0_to_f32(sw[blk] & 0xffu);
+          sc[blk][1] = e8m0_to_f32((sw[blk] >> 8) & 0xffu);
         }
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
           bf16x8_t af[NMT];
+          const int off = a_rd + 8 * (p ^ (xr & 7));
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt)
-            af[mt] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][32 * MTW * wm + 32 * mt + r32][64 * g + 8 * p]);
+            af[mt] = *reinterpret_cast<const bf16x8_t*>(rd + (32 * MTW * wm + 32 * mt) * kKT + off);
 #pragma unroll
           for (int blk = 0; blk < 2; ++blk) {
             const bf16x8_t bf = fp4_to_bf16x8(b_use.c[blk][p >> 2][p & 3], sc[blk][p >> 2]);
@@ -445,19 +502,38 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
           }
         }
       }
-      store_a(a_reg, buf ^ 1);  // after the last step: unused, harmless
+      vmem_wait_all();  // this wave's direct-to-LDS loads have landed
       lds_barrier();
     };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     load_b(b_reg0, 0);
-    load_a(a_reg, 0);
-    store_a(a_reg, 0);
+    if constexpr (SCS > 1) load_sn(0);
+    load_a(s_a0, 0);
+    vmem_wait_all();
     lds_barrier();
-    int ks = 0;
-    for (; ks + 2 <= nsteps; ks += 2) {
-      step(ks, b_reg0, b_reg1);
-      step(ks + 1, b_reg1, b_reg0);
+    if constexpr (SCS == 2) {  // nsteps % 2 == 0
+      for (int ks = 0; ks < nsteps; ks += 2) {
+        step(I0{}, ks, b_reg0, b_reg1);
+        step(I1{}, ks + 1, b_reg1, b_reg0);
+      }
+    } else if constexpr (SCS == 4) {  // nsteps % 4 == 0
+      for (int ks = 0; ks < nsteps; ks += 4) {
+        step(I0{}, ks, b_reg0, b_reg1);
+        step(I1{}, ks + 1, b_reg1, b_reg0);
+        step(I2{}, ks + 2, b_reg0, b_reg1);
+        step(I3{}, ks + 3, b_reg1, b_reg0);
+      }
+    } else {
+      int ks = 0;
+      for (; ks + 2 <= nsteps; ks += 2) {
+        step(I0{}, ks, b_reg0, b_reg1);
+        step(I1{}, ks + 1, b_reg1, b_reg0);
+      }
+      if (ks < nsteps) step(I0{}, ks, b_reg0, b_reg1);
     }
-    if (ks < nsteps) step(ks, b_reg0, b_reg1);
   };
   if constexpr (MTW == 4) {
     switch (nmt) {
@@ -965,8 +1041,16 @@ static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   const QMat& m = a.m0;
   if (m.fmt == 1 && QSMOE_MXFP4_W && m.rows % ((GATEUP ? 32 : 64) * MXW_WN) == 0) {
     const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
-    QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP>),
-                 dim3(mfma_grid(a.T, a.k, a.E, m.rows, (GATEUP ? 32 : 64) * MXW_WN, 128)), dim3(256), lds, s, a);
+    const dim3 grid(mfma_grid(a.T, a.k, a.E, m.rows, (GATEUP ? 32 : 64) * MXW_WN, 128));
+    // scale loads of SCS steps (4 SCS bytes) need rows of whole chunks on aligned scale arrays
+    constexpr int SCS = QSMOE_MXFP4_SCS;
+    const bool chunked = SCS > 1 && m.cols % (SCS * kKT) == 0 &&
+                         reinterpret_cast<uintptr_t>(a.m0.scales) % (4 * SCS) == 0 &&
+                         reinterpret_cast<uintptr_t>(a.m1.scales) % (4 * SCS) == 0;
+    if (chunked)
+      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, SCS>), grid, dim3(256), lds, s, a);
+    else
+      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 1>), grid, dim3(256), lds, s, a);
   } else if (m.fmt == 1) {
     // measured: gate/up best with 128-token tiles x 32 columns per wave, down
     // with 64-token tiles x 64 columns per wave
