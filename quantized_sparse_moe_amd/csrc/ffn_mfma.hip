@@ -72,6 +72,18 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds) {
 // s_waitcnt vmcnt(0), leaving the LDS/scalar and export counters alone
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Workgroup barrier that leaves the wave's 4 newest vector loads in flight:
+// s_waitcnt vmcnt(4) lgkmcnt(0), then s_barrier between compiler-only fences
+// (they keep LDS accesses from moving across; a release fence would make the
+// wave wait for every load in flight, since the compiler cannot tell
+// direct-to-LDS loads from register loads). Loads complete in order, so
+// everything older than the 4 newest has landed.
+__device__ __forceinline__ void barrier_keep4() {
+  __builtin_amdgcn_s_waitcnt(0x0074);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 __device__ __forceinline__ bf16x8_t fp4_to_bf16x8(uint32_t word, float scale) {
   uint32_t r[4];
@@ -97,7 +109,7 @@ template <int MT>
 __device__ bool tile_of_block(const MfmaArgs& a, int n_ntiles, int32_t* s_off, int32_t* s_mt, Tile& t) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int n = a.T * a.k;
-  for (int i = tid; i <= a.E; i += 256) s_off[i] = a.shared ? (i == 0 ? 0 : n) : min(max(a.offsets[i], 0), n);
+  for (int i = tid; i <= a.E; i += blockDim.x) s_off[i] = a.shared ? (i == 0 ? 0 : n) : min(max(a.offsets[i], 0), n);
   __syncthreads();
   if (wave == 0) {
     int carry = 0;
@@ -315,15 +327,17 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   }
 }
 
-#ifndef MXW_WN
-#define MXW_WN 4  // waves along the output rows (4: each wave takes all 128 tokens)
+#ifndef QSMOE_MXW_NW
+#define QSMOE_MXW_NW 4  // waves per workgroup in k_mfma_mxfp4_w (4: two workgroups per CU, or 8: one)
 #endif
-#define MXW_MT (4 / (4 / MXW_WN))
 #ifndef QSMOE_MXW_PIN_LOADS
 #define QSMOE_MXW_PIN_LOADS 1
 #endif
+#ifndef QSMOE_MXW_DEEP
+#define QSMOE_MXW_DEEP 1  // 4-deep weight ring in k_mfma_mxfp4_w for tiles of under 4 token blocks
+#endif
 #ifndef QSMOE_MXFP4_SCS
-#define QSMOE_MXFP4_SCS 2  // K steps per scale load in k_mfma_mxfp4_w (1, 2 or 4)
+#define QSMOE_MXFP4_SCS 4  // most K steps per scale load in k_mfma_mxfp4_w (1, 2 or 4)
 #endif
 
 // ---------------------------------------------------------------------------
@@ -346,14 +360,13 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 // cover them. Per pass a wave reads 4 activation fragments from LDS and
 // converts 2 weight fragments for 8 MFMAs of 32 x 32 x 16.
 template <bool GATEUP, int SCS>
-__global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
+__global__ __launch_bounds__(64 * QSMOE_MXW_NW, 8 / QSMOE_MXW_NW) void k_mfma_mxfp4_w(MfmaArgs a) {
   typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+  constexpr int NW = QSMOE_MXW_NW;
   constexpr int MT = 128;
-  constexpr int MTW = MXW_MT;                // 32-token tiles per wave
-  constexpr int WM = 4 / MXW_WN;             // waves along the tokens
-  constexpr int NTILE = (GATEUP ? 32 : 64) * MXW_WN;  // output rows per workgroup (per matrix)
-  static_assert(WM * MTW * 32 == 128, "the waves along M cover the 128-token tile");
-  constexpr int ACH = MT * 16 / 256;        // 16-byte activation chunks per thread per K step
+  constexpr int MTW = MT / 32;                   // 32-token tiles per wave
+  constexpr int NTILE = (GATEUP ? 32 : 64) * NW;  // output rows per workgroup (per matrix)
+  constexpr int ACH = MT * 16 / (64 * NW);       // 16-byte activation chunks per thread per K step
   extern __shared__ int32_t s_dyn[];        // expert offsets and m-tile starts, E + 1 each
   int32_t* const s_off = s_dyn;
   int32_t* const s_mt = s_dyn + a.E + 1;
@@ -365,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int g = lane >> 5, r32 = lane & 31;
-  const int wm = wave % WM, wn = wave / WM;
+  const int wn = wave;
   const int n = a.T * a.k;
   const int rows = a.m0.rows, cols = a.m0.cols;
   Tile t;
@@ -379,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
   __syncthreads();
 
   // activations: direct global -> LDS loads, 16 bytes per lane. Round i of
-  // wave w fills the 1 KB of tile rows 4 b .. 4 b + 3, b = 8 w + i: lane l
+  // wave w fills the 1 KB of tile rows 4 b .. 4 b + 3, b = ACH w + i: lane l
   // writes slot l % 16 of row 4 b + l / 16 (rows of 256 bytes, unpadded), and
   // slot s of row r holds input chunk s ^ (r % 16) of the step, so the 16
   // rows that 16 lanes read at once hold a chunk in 16 different slots (no
@@ -429,49 +442,75 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
       if constexpr (SCS == 1) b.s[blk] = *reinterpret_cast<const uint16_t*>(sb[blk] + k0 / 32 + 2 * g);
     }
   };
-  // SCS > 1: the e8m0 bytes of SCS K steps in one 4 SCS-byte load per
-  // block (byte 4 j + 2 g + h = group 2 g + h of step j), issued one step
-  // before the first of them is needed. A 2-byte load per lane and step
-  // costs about as much as a 16-byte one: each touches 32 rows' cache lines.
-  typedef __attribute__((ext_vector_type(SCS == 1 ? 1 : SCS))) uint32_t scv_t;
-  scv_t scn[2];
-  auto load_sn = [&](int k0) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) scn[blk] = *reinterpret_cast<const scv_t*>(sb[blk] + k0 / 32);
-  };
 
-  f32x16_t acc[MTW][2];
-#pragma unroll
-  for (int i = 0; i < MTW; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-
-  const int nmt = min(MTW, max(0, (count - 32 * MTW * wm + 31) / 32));  // this wave's 32-token tiles with tokens
+  const int nmt = min(MTW, (count + 31) / 32);  // 32-token tiles with tokens
   const int nsteps = cols / kKT;
-  // activations and weights one K step ahead (a step is ~2000 MFMA cycles
-  // per wave); weights in a register ring
-  BRegs b_reg0, b_reg1;
-  auto kloop = [&](auto nmt_tag) {
+  // Activations one K step ahead in LDS; weights D - 1 steps ahead in a
+  // register ring of D. D = 4 where the accumulators leave the registers
+  // (under 4 token blocks with tokens) and the scales come in 4-step chunks;
+  // since loads complete in order and every step waits for its activation
+  // loads, a weight load then has two steps to land instead of one.
+  auto kloop = [&](auto nmt_tag, auto d_tag) {
     constexpr int NMT = decltype(nmt_tag)::value;
-    // J: the step's place in its group of 4 (its parity picks the buffers;
-    // J % SCS is its place in its scale chunk)
-    auto step = [&](auto j_tag, int ks, const BRegs& b_use, BRegs& b_ld) {
+    constexpr int D = decltype(d_tag)::value;
+    static_assert(D == 2 || (D == 4 && SCS == 4), "a 4-deep ring takes 4-step scale chunks");
+    // CS > 1: the e8m0 bytes of CS K steps in one 4 CS-byte load per block
+    // (byte 4 j + 2 g + h = group 2 g + h of step j), issued one step (D = 2)
+    // or four steps (D = 4) before the first of them is needed. A 2-byte load
+    // per lane and step costs about as much as a 16-byte one: each touches
+    // 32 rows' cache lines. (With all 4 token blocks, 4-step chunks and a
+    // 2-deep ring exceed the registers.)
+    constexpr int CS = D == 4 ? 4 : (SCS < 2 ? SCS : 2);
+    typedef __attribute__((ext_vector_type(CS))) uint32_t scv_t;
+    scv_t scn[2], s_nxt[2];  // the current chunk; D == 4: the next one
+    auto load_sn = [&](scv_t (&dst)[2], int k0) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) dst[blk] = *reinterpret_cast<const scv_t*>(sb[blk] + k0 / 32);
+    };
+    // a wave whose activation rows all lie in 32-token blocks without tokens
+    // (their MFMAs are skipped) loads nothing
+    const bool a_need = 4 * ACH * wave < 32 * NMT;
+    // accumulators of the token blocks with tokens only (the others would
+    // hold registers through the whole loop)
+    f32x16_t acc[NMT > 0 ? NMT : 1][2];
+#pragma unroll
+    for (int i = 0; i < (NMT > 0 ? NMT : 1); ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+    BRegs ring[D];
+    // J: the step's place in the unrolled group (its parity picks the LDS
+    // buffers; J % CS is its place in its scale chunk, J % D its ring slot)
+    auto step = [&](auto j_tag, int ks) {
       constexpr int J = decltype(j_tag)::value;
+      const BRegs& b_use = ring[J % D];
+      BRegs& b_ld = ring[(J + D - 1) % D];
       uint16_t* const rd = (J & 1) ? s_a1 : s_a0;
       uint16_t* const wr = (J & 1) ? s_a0 : s_a1;
       const int kn = min(ks + 1, nsteps - 1) * kKT;
+      const int kb = min(ks + D - 1, nsteps - 1) * kKT;
       uint32_t sw[2];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        if constexpr (SCS == 1)
+        if constexpr (CS == 1)
           sw[blk] = b_use.s[blk];
         else
-          sw[blk] = scn[blk][J % SCS] >> (16 * g);
+          sw[blk] = scn[blk][J % CS] >> (16 * g);
       }
-      load_a(wr, kn);  // after the last step: unused, harmless
-      load_b(b_ld, kn);
-      if constexpr (SCS > 1 && J % SCS == SCS - 1) {
-        if (ks + 1 < nsteps) load_sn(kn);
+      if constexpr (D == 2) {
+        if (a_need) load_a(wr, kn);  // after the last step: unused, harmless
+        load_b(b_ld, kb);
+        if constexpr (CS > 1 && J % CS == CS - 1) {
+          if (ks + 1 < nsteps) load_sn(scn, kn);
+        }
+      } else {
+        // order: next scale chunk, activations, weights; the end-of-step wait
+        // then leaves exactly the 4 weight loads in flight
+        if constexpr (J == 0) {
+          if (ks + 4 < nsteps) load_sn(s_nxt, (ks + 4) * kKT);
+        }
+        if (a_need) load_a(wr, kn);
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(b_ld, kb);
       }
 #if QSMOE_MXW_PIN_LOADS
       // keep the next step's loads at the top of this one: left to itself the
@@ -492,7 +531,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
           const int off = a_rd + 8 * (p ^ (xr & 7));
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt)
-            af[mt] = *reinterpret_cast<const bf16x8_t*>(rd + (32 * MTW * wm + 32 * mt) * kKT + off);
+            af[mt] = *reinterpret_cast<const bf16x8_t*>(rd + 32 * mt * kKT + off);
 #pragma unroll
           for (int blk = 0; blk < 2; ++blk) {
             const bf16x8_t bf = fp4_to_bf16x8(b_use.c[blk][p >> 2][p & 3], sc[blk][p >> 2]);
@@ -502,74 +541,75 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
           }
         }
       }
-      vmem_wait_all();  // this wave's direct-to-LDS loads have landed
-      lds_barrier();
+      if constexpr (D == 4 && J == 3) {
+        scn[0] = s_nxt[0];
+        scn[1] = s_nxt[1];
+      }
+      if constexpr (D == 2) {
+        vmem_wait_all();  // this wave's direct-to-LDS loads (and the next weights) have landed
+        lds_barrier();
+      } else {
+        barrier_keep4();  // all but this step's 4 weight loads: the activations have landed
+      }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-    load_b(b_reg0, 0);
-    if constexpr (SCS > 1) load_sn(0);
-    load_a(s_a0, 0);
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(i, nsteps - 1) * kKT);
+    if constexpr (CS > 1) load_sn(scn, 0);
+    if (a_need) load_a(s_a0, 0);
     vmem_wait_all();
     lds_barrier();
-    if constexpr (SCS == 2) {  // nsteps % 2 == 0
+    if constexpr (CS == 2) {  // nsteps % 2 == 0
       for (int ks = 0; ks < nsteps; ks += 2) {
-        step(I0{}, ks, b_reg0, b_reg1);
-        step(I1{}, ks + 1, b_reg1, b_reg0);
+        step(I0{}, ks);
+        step(I1{}, ks + 1);
       }
-    } else if constexpr (SCS == 4) {  // nsteps % 4 == 0
+    } else if constexpr (CS == 4) {  // nsteps % 4 == 0
       for (int ks = 0; ks < nsteps; ks += 4) {
-        step(I0{}, ks, b_reg0, b_reg1);
-        step(I1{}, ks + 1, b_reg1, b_reg0);
-        step(I2{}, ks + 2, b_reg0, b_reg1);
-        step(I3{}, ks + 3, b_reg1, b_reg0);
+        step(I0{}, ks);
+        step(I1{}, ks + 1);
+        step(I2{}, ks + 2);
+        step(I3{}, ks + 3);
       }
     } else {
       int ks = 0;
       for (; ks + 2 <= nsteps; ks += 2) {
-        step(I0{}, ks, b_reg0, b_reg1);
-        step(I1{}, ks + 1, b_reg1, b_reg0);
+        step(I0{}, ks);
+        step(I1{}, ks + 1);
       }
-      if (ks < nsteps) step(I0{}, ks, b_reg0, b_reg1);
+      if (ks < nsteps) step(I0{}, ks);
+    }
+
+    // epilogue: element i of lane l is token 32 mt + 8 (i / 4) + 4 g + i % 4
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tl = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (tl >= count) continue;
+        if constexpr (GATEUP) {
+          a.h[static_cast<size_t>(p0 + tl) * rows + row0] =
+              static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mt][0][i]) * acc[mt][1][i]));
+        } else {
+          const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
+          float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
+          yrow[0] = acc[mt][0][i];
+          yrow[32] = acc[mt][1][i];
+        }
+      }
     }
   };
-  if constexpr (MTW == 4) {
-    switch (nmt) {
-      case 4: kloop(std::integral_constant<int, 4>{}); break;
-      case 3: kloop(std::integral_constant<int, 3>{}); break;
-      case 2: kloop(std::integral_constant<int, 2>{}); break;
-      case 1: kloop(std::integral_constant<int, 1>{}); break;
-      default: kloop(std::integral_constant<int, 0>{}); break;
-    }
-  } else {
-    if (nmt == 2)
-      kloop(std::integral_constant<int, 2>{});
-    else if (nmt == 1)
-      kloop(std::integral_constant<int, 1>{});
-    else
-      kloop(std::integral_constant<int, 0>{});
-  }
-
-  // epilogue: element i of lane l is token 32 MTW wm + 32 mt + 8 (i / 4) + 4 g + i % 4
-#pragma unroll
-  for (int mt = 0; mt < MTW; ++mt) {
-    if (mt >= nmt) continue;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int tl = 32 * MTW * wm + 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (tl >= count) continue;
-      if constexpr (GATEUP) {
-        a.h[static_cast<size_t>(p0 + tl) * rows + row0] =
-            static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mt][0][i]) * acc[mt][1][i]));
-      } else {
-        const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
-        float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
-        yrow[0] = acc[mt][0][i];
-        yrow[32] = acc[mt][1][i];
-      }
-    }
+  using D2 = std::integral_constant<int, 2>;
+  using D4 = std::integral_constant<int, (SCS == 4 && QSMOE_MXW_DEEP) ? 4 : 2>;
+  switch (nmt) {
+    case 4: kloop(std::integral_constant<int, 4>{}, D2{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}, D2{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}, D4{}); break;
+    case 1: kloop(std::integral_constant<int, 1>{}, D4{}); break;
+    default: kloop(std::integral_constant<int, 0>{}, D2{}); break;
   }
 }
 
@@ -1039,18 +1079,23 @@ static void launch_affine(const MfmaArgs& a, hipStream_t s) {
 template <bool GATEUP>
 static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   const QMat& m = a.m0;
-  if (m.fmt == 1 && QSMOE_MXFP4_W && m.rows % ((GATEUP ? 32 : 64) * MXW_WN) == 0) {
+  constexpr int kMxwN = (GATEUP ? 32 : 64) * QSMOE_MXW_NW;  // k_mfma_mxfp4_w's rows per workgroup
+  if (m.fmt == 1 && QSMOE_MXFP4_W && m.rows % kMxwN == 0) {
     const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
-    const dim3 grid(mfma_grid(a.T, a.k, a.E, m.rows, (GATEUP ? 32 : 64) * MXW_WN, 128));
-    // scale loads of SCS steps (4 SCS bytes) need rows of whole chunks on aligned scale arrays
-    constexpr int SCS = QSMOE_MXFP4_SCS;
-    const bool chunked = SCS > 1 && m.cols % (SCS * kKT) == 0 &&
-                         reinterpret_cast<uintptr_t>(a.m0.scales) % (4 * SCS) == 0 &&
-                         reinterpret_cast<uintptr_t>(a.m1.scales) % (4 * SCS) == 0;
-    if (chunked)
-      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, SCS>), grid, dim3(256), lds, s, a);
+    const dim3 grid(mfma_grid(a.T, a.k, a.E, m.rows, kMxwN, 128));
+    // scale loads of c steps (4 c bytes) need rows of whole chunks on aligned scale arrays
+    auto chunks = [&](int c) {
+      return c <= QSMOE_MXFP4_SCS && m.cols % (c * kKT) == 0 &&
+             reinterpret_cast<uintptr_t>(a.m0.scales) % (4 * c) == 0 &&
+             reinterpret_cast<uintptr_t>(a.m1.scales) % (4 * c) == 0;
+    };
+    const dim3 block(64 * QSMOE_MXW_NW);
+    if (chunks(4))
+      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 4>), grid, block, lds, s, a);
+    else if (chunks(2))
+      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 2>), grid, block, lds, s, a);
     else
-      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 1>), grid, dim3(256), lds, s, a);
+      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 1>), grid, block, lds, s, a);
   } else if (m.fmt == 1) {
     // measured: gate/up best with 128-token tiles x 32 columns per wave, down
     // with 64-token tiles x 64 columns per wave
