@@ -687,10 +687,25 @@ constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
 #ifndef QSMOE_AFF_MINWG
 #define QSMOE_AFF_MINWG 2
 #endif
+#ifndef QSMOE_AFF_NT
+#define QSMOE_AFF_NT 1
+#endif
+#ifndef QSMOE_AFF_MINWG3_G64
+#define QSMOE_AFF_MINWG3_G64 1
+#endif
 
+
+// workgroups per CU the register budget is cut for: 3 (168 VGPRs) for the
+// 4-bit, 64-group, 16-token down projection, which needs only a few more
+// (measured: 304 -> 294 us at 512 tokens; the gate/up one spills more and
+// got slower, 626 -> 647 us), else QSMOE_AFF_MINWG
+template <bool GATEUP, int BITS, int G, int MT>
+constexpr int aff_min_wg() {
+  return (QSMOE_AFF_MINWG3_G64 && !GATEUP && BITS == 4 && G == 64 && MT == 16) ? 3 : QSMOE_AFF_MINWG;
+}
 
 template <bool GATEUP, int BITS, int G, int MT>
-__global__ __launch_bounds__(256, QSMOE_AFF_MINWG) void k_mfma_affine(MfmaArgs a) {
+__global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mfma_affine(MfmaArgs a) {
   constexpr int RB = kAffRB;
   constexpr int HB = GATEUP ? RB / 2 : RB;           // row blocks per matrix per wave
   constexpr int NTILE = 4 * HB * 16;                 // rows per matrix per workgroup
@@ -788,7 +803,15 @@ __global__ __launch_bounds__(256, QSMOE_AFF_MINWG) void k_mfma_affine(MfmaArgs a
       const int rb = RPI * i / 16;
       const char* p = (rb >= HB ? cb1 : cb0) + static_cast<size_t>(16 * (rb % HB) + RPI * i % 16) * row_bytes + o;
       if constexpr (BW == 4) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+        // gate/up codes non-temporally (measured at 512 tokens: 4-bit gate/up
+        // 630 -> 587 us, 2-bit at 64 tokens 290 -> 278 us; the down
+        // projection, whose weights more m-tiles share, got slower, and so
+        // did the MXFP4 GEMM, which re-reads each expert per 128 tokens)
+        u32x4_t v;
+        if constexpr (GATEUP && QSMOE_AFF_NT)
+          v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+        else
+          v = *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
         for (int w = 0; w < 4; ++w) stg[i][w] = v[w];
       } else {
@@ -880,7 +903,9 @@ __global__ __launch_bounds__(256, QSMOE_AFF_MINWG) void k_mfma_affine(MfmaArgs a
       const int buf = ks & 1;
       if constexpr (JM == 0) {
         // a macro step begins: its staged codes go to the wave's LDS slot and
-        // the next macro step's loads are issued
+        // the next macro step's loads are issued (two macro steps in flight,
+        // in a second set of staging registers, measured slower: 631 -> 656
+        // us for the 4-bit gate/up at 512 tokens)
         store_macro();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
         __builtin_amdgcn_wave_barrier();
