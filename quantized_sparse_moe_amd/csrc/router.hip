@@ -219,23 +219,26 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 }
 
 // ---------------------------------------------------------------------------
-// Hash route: one wave per token. ids from tid2eid[token], logits of those k
-// experts, sqrtsoftplus, renormalised weights. Out-of-range token ids or
-// table entries set the device error word; the id becomes 0 and the token's
-// weights 0 so every access stays in bounds.
+// Hash route: one workgroup per token. ids from tid2eid[token], logits of
+// those k experts (the 4 waves take interleaved 512-input slices of the
+// hidden dimension and their partial sums meet in LDS), sqrtsoftplus,
+// renormalised weights. Out-of-range token ids or table entries set the
+// device error word; the id becomes 0 and the token's weights 0 so every
+// access stays in bounds. (One wave per token walked its 6 router rows in
+// 8 dependent rounds: 24 us for 512 tokens.)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, const float* __restrict__ wr,
                                               const int32_t* __restrict__ token_ids,
                                               const int32_t* __restrict__ tid2eid, int T, int E, int k, int d,
                                               int vocab, float routed_scale, int32_t* __restrict__ ids,
                                               float* __restrict__ w, int32_t* err) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ float s_part[4][8];
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
   int tok = token_ids[t];
   bool ok = true;
   if (tok < 0 || tok >= vocab) {
-    if (lane == 0) set_device_error(err, 1);
+    if (threadIdx.x == 0) set_device_error(err, 1);
     tok = 0;
     ok = false;
   }
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
     if (j < k) {
       int e = tid2eid[static_cast<size_t>(tok) * k + j];
       if (e < 0 || e >= E) {
-        if (lane == 0) set_device_error(err, 2);
+        if (threadIdx.x == 0) set_device_error(err, 2);
         e = 0;
         ok = false;
       }
@@ -256,7 +259,8 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
     }
   }
   const uint16_t* xr = x + static_cast<size_t>(t) * d;
-  for (int base = lane * 8; base < d; base += 64 * 8) {
+#pragma unroll 2
+  for (int base = threadIdx.x * 8; base < d; base += 256 * 8) {
     const uint4 xv = *reinterpret_cast<const uint4*>(xr + base);
     const float xf[8] = {bf16_to_f32(xv.x & 0xffffu), bf16_to_f32(xv.x >> 16), bf16_to_f32(xv.y & 0xffffu),
                          bf16_to_f32(xv.y >> 16),     bf16_to_f32(xv.z & 0xffffu), bf16_to_f32(xv.z >> 16),
@@ -280,13 +284,18 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
       }
     }
   }
-  float tot[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) tot[j] = wave_sum(acc[j]);
+  for (int j = 0; j < 8; ++j) {
+    const float p = wave_sum(acc[j]);
+    if (lane == 0) s_part[wave][j] = p;
+  }
+  __syncthreads();
+  if (wave != 0) return;
   float s[8], total = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    s[j] = j < k ? sqrtsoftplus(tot[j]) : 0.0f;
+    const float tot = (s_part[0][j] + s_part[1][j]) + (s_part[2][j] + s_part[3][j]);
+    s[j] = j < k ? sqrtsoftplus(tot) : 0.0f;
     total += s[j];
   }
   if (lane < k) {
@@ -333,8 +342,9 @@ hipError_t launch_router_topk(const float* logits, const float* bias, int T, int
 hipError_t launch_router_hash(const uint16_t* x, const float* wr, const int32_t* token_ids,
                               const int32_t* tid2eid, int T, int E, int k, int d, int vocab, float routed_scale,
                               int32_t* ids, float* w, int32_t* err, hipStream_t s) {
-  QSMOE_LAUNCH(k_hash, dim3((T + 3) / 4), dim3(256), 0, s, x, wr, token_ids, tid2eid, T, E, k, d, vocab,
-                     routed_scale, ids, w, err);
+  if (T == 0) return hipSuccess;
+  QSMOE_LAUNCH(k_hash, dim3(T), dim3(256), 0, s, x, wr, token_ids, tid2eid, T, E, k, d, vocab, routed_scale, ids,
+               w, err);
   return hipGetLastError();
 }
 
