@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=16)
-    p.add_argument("--workload", default="decode", choices=["decode", "tiny", "hash", "prefill", "mixed"])
+    p.add_argument("--workload", default="decode", choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8"])
     p.add_argument("--copies", type=int, default=0, help="device copies of the layer to rotate over (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
@@ -50,7 +50,9 @@ def parse():
 
 def workload_text(cfg) -> str:
     def fmt(f):
-        return "mxfp4 e2m1+e8m0/32" if f.fmt == "mxfp4" else f"affine {f.bits}-bit g{f.group}"
+        if f.fmt in ("mxfp4", "mxfp8"):
+            return f"{f.fmt} {'e2m1' if f.fmt == 'mxfp4' else 'e4m3'}+e8m0/32"
+        return f"affine {f.bits}-bit g{f.group}"
     s = (f"{cfg.name}: T={cfg.T} tokens/step, d={cfg.d}, I={cfg.I}, E={cfg.E}, top-{cfg.top_k} "
          f"{'tid2eid hash' if cfg.route == 'hash' else 'sqrtsoftplus+bias'} routing, gate/up {fmt(cfg.gate_up)}, "
          f"down {fmt(cfg.down)}")

@@ -58,7 +58,7 @@ typedef enum {
   MOE_ERR_HIP = -5          /* a HIP launch or runtime call failed             */
 } moe_status;
 
-typedef enum { MOE_FMT_AFFINE = 0, MOE_FMT_MXFP4 = 1 } moe_format;
+typedef enum { MOE_FMT_AFFINE = 0, MOE_FMT_MXFP4 = 1, MOE_FMT_MXFP8 = 2 } moe_format;
 typedef enum { MOE_ROUTE_TOPK = 0, MOE_ROUTE_HASH = 1 } moe_route_mode;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
 
@@ -89,6 +89,18 @@ typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
  * (OCP MX e2m1), times 2^(s - 127) for the row's scale byte s of that group of
  * 32 (s = 255 is NaN).  bits = 4, g = 32.
  *   codes  : uint32 [E][rows][cols / 8]
+ *   scales : uint8  [E][rows][cols / 32]
+ *   biases : NULL
+ *
+ * MOE_FMT_MXFP8 ([PR1192] FP8-to-bf16 requantization report: E4M3 bytes
+ * viewed as uint32 words with E8M0 block scales expanded to one per 32, read
+ * by mx.dequantize with group_size 32, bits 8, mode "mxfp8"; [PR1190]:
+ * MXFP8-quantized MoE layers, F8_E4M3 kept as uint8): byte j of a row holds
+ * element j as OCP FP8 E4M3 (bit 7 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; exponent 0 subnormal; S.1111.111 NaN; largest 448), times
+ * 2^(s - 127) for the row's scale byte s of that group of 32.  bits = 8,
+ * g = 32.
+ *   codes  : uint32 [E][rows][cols / 4]
  *   scales : uint8  [E][rows][cols / 32]
  *   biases : NULL
  *

@@ -13,7 +13,7 @@ Sources (web pages, cited by title and section):
   [SERVE]   model card "DeepSeek-V4-Flash-0731-MLX-Serve-mixed-2-3-8bit"
 
 Readings taken where the pages are silent or ambiguous (each marked READING
-below): e2m1 bit layout and e8m0 0xFF = NaN from the public OCP MX format;
+below): e2m1 and e4m3 bit layouts and e8m0 0xFF = NaN from the public OCP MX format;
 nibble/bit order LSB-first along the input dimension; the router bias only
 ranks experts and does not enter the combine weights; hash-routed layers have
 no bias; ties in the top-k go to the lower expert index and the k slots are
@@ -36,7 +36,7 @@ from types import SimpleNamespace
 import numpy as np
 
 __all__ = [
-    "bf16_bits_to_f64", "round_bf16", "e2m1_decode", "e8m0_decode", "unpack_codes",
+    "bf16_bits_to_f64", "round_bf16", "e2m1_decode", "e4m3_decode", "e8m0_decode", "unpack_codes",
     "dequant", "sqrtsoftplus", "silu", "router_logits", "route_topk", "route_hash",
     "combine_weights_for_ids", "permute", "swiglu_expert", "forward", "forward_tokens",
 ]
@@ -86,6 +86,25 @@ def e2m1_decode(nibbles) -> np.ndarray:
     return sign * mag
 
 
+def e4m3_decode(codes) -> np.ndarray:
+    """FP8 e4m3 code -> value.
+
+    [PR1192] (FP8-to-bf16 requantization report) names the weight bytes FP8
+    E4M3 and reads them with mx.dequantize in "mxfp8" mode; [PR1190] calls
+    the layers MXFP8-quantized. READING: the OCP E4M3 layout ("e4m3fn") --
+    bit 7 sign, bits 6..3 exponent (bias 7), bits 2..0 mantissa; exponent 0
+    is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities, so the
+    largest magnitude is 1.75 * 2^8 = 448.
+    """
+    n = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(n & 0x80, -1.0, 1.0)
+    exp = (n >> 3) & 0xF
+    man = (n & 7).astype(np.float64)
+    mag = np.where(exp == 0, np.ldexp(man / 8.0, -6), np.ldexp(1.0 + man / 8.0, exp - 7))
+    mag = np.where((n & 0x7F) == 0x7F, np.nan, mag)
+    return sign * mag
+
+
 def e8m0_decode(b) -> np.ndarray:
     """e8m0 scale byte -> 2^(b - 127) ([PR1190] description: F8_E8M0 decoded as
     unsigned exponents). READING: 0xFF is NaN per OCP MX."""
@@ -123,6 +142,9 @@ def dequant(q, e: int = 0) -> np.ndarray:
     mxfp4:  w = e2m1(code) * 2^(scale_byte - 127), one scale byte per 32
             inputs ([PR1192] dequantize call with group_size=32, bits=4,
             mode="mxfp4"; e8m0 per [PR1190]).
+    mxfp8:  w = e4m3(code) * 2^(scale_byte - 127), one byte per code and one
+            scale byte per 32 inputs ([PR1192] requantization report:
+            mx.dequantize with group_size=32, bits=8, mode="mxfp8").
     """
     spec = q.spec
     codes = unpack_codes(q.codes[e], spec.bits, q.cols)            # [rows][cols]
@@ -133,6 +155,9 @@ def dequant(q, e: int = 0) -> np.ndarray:
     if spec.fmt == "mxfp4":
         scale = np.repeat(e8m0_decode(q.scales[e]), 32, axis=-1)
         return e2m1_decode(codes) * scale
+    if spec.fmt == "mxfp8":
+        scale = np.repeat(e8m0_decode(q.scales[e]), 32, axis=-1)
+        return e4m3_decode(codes) * scale
     raise ValueError(spec.fmt)
 
 

@@ -20,6 +20,7 @@ MOE_ERR_HIP = -5
 
 MOE_FMT_AFFINE = 0
 MOE_FMT_MXFP4 = 1
+MOE_FMT_MXFP8 = 2
 MOE_ROUTE_TOPK = 0
 MOE_ROUTE_HASH = 1
 MOE_OUT_BF16 = 0

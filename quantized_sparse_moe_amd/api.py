@@ -51,7 +51,8 @@ class DeviceQTensor:
         self.fmt, self.bits, self.group, self.rows, self.cols = fmt, bits, group, rows, cols
         self.codes, self.scales, self.biases = codes, scales, biases
         self.num_experts = codes.shape[0]
-        self.c = QTensorC(_lib.MOE_FMT_AFFINE if fmt == "affine" else _lib.MOE_FMT_MXFP4, bits, group, rows, cols,
+        fmt_c = {"affine": _lib.MOE_FMT_AFFINE, "mxfp4": _lib.MOE_FMT_MXFP4, "mxfp8": _lib.MOE_FMT_MXFP8}[fmt]
+        self.c = QTensorC(fmt_c, bits, group, rows, cols,
                           self.num_experts, codes.data_ptr(), scales.data_ptr(),
                           biases.data_ptr() if biases is not None else None)
 

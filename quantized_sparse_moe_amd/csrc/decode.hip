@@ -419,6 +419,9 @@ static unsigned dec_grid(int64_t units, int min_rows = 2) {
   } else if ((FMT_) == 0 && (BITS_) == 8) {                  \
     constexpr int F = 0, B = 8;                              \
     __VA_ARGS__                                              \
+  } else if ((FMT_) == 2) {                                  \
+    constexpr int F = 2, B = 8;                              \
+    __VA_ARGS__                                              \
   } else {                                                   \
     constexpr int F = 1, B = 4;                              \
     __VA_ARGS__                                              \

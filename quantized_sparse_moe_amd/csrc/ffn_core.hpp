@@ -104,6 +104,23 @@ struct Codec<1, 4> {
   }
 };
 
+// MXFP8: byte b of word j holds code 4j+b (OCP E4M3); pair m = 2j + h is
+// (4j+2h, 4j+2h+1). Every finite E4M3 value is exact in bf16, so the scaled
+// conversion runs with scale 1 and the e8m0 scale multiplies the dot product.
+template <>
+struct Codec<2, 8> {
+  static constexpr float kOff = 0.0f;
+  static constexpr int lo(int m) { return 2 * m; }
+  static constexpr int hi(int m) { return 2 * m + 1; }
+  __device__ static __forceinline__ void pairs(const uint32_t (&w)[8], uint32_t (&p)[16]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[2 * j + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, false));
+      p[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[j], 1.0f, true));
+    }
+  }
+};
+
 // Activations of NT tokens for the lane's CPL chunks.
 template <int FMT, int BITS, int CPL, int NT>
 struct XRegs {

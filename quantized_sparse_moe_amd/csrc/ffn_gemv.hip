@@ -39,6 +39,7 @@ static int chunks_per_lane(int cols) { return cols <= 2048 ? 1 : (cols <= 4096 ?
 bool gemv_supported(const QMat& m) {
   if (m.cols % 32 != 0 || m.cols > 8192 || m.rows < 1) return false;
   if (m.fmt == 0) return m.bits == 2 || m.bits == 3 || m.bits == 4 || m.bits == 8;
+  if (m.fmt == 2) return m.bits == 8 && m.group == 32;
   return m.fmt == 1 && m.bits == 4 && m.group == 32;
 }
 
@@ -67,6 +68,9 @@ static int tokens_per_pass(int T, int k, int E, int cpl, int shared) {
     __VA_ARGS__                                              \
   } else if ((FMT_) == 0 && (BITS_) == 8) {                  \
     constexpr int F = 0, B = 8;                              \
+    __VA_ARGS__                                              \
+  } else if ((FMT_) == 2) {                                  \
+    constexpr int F = 2, B = 8;                              \
     __VA_ARGS__                                              \
   } else {                                                   \
     constexpr int F = 1, B = 4;                              \

@@ -677,6 +677,20 @@ __device__ __forceinline__ bf16x8_t chunk_to_bf16x8(const uint32_t (&f)[BITS == 
   }
 }
 
+// MXFP8: a chunk of 8 E4M3 codes (code i in byte i % 4 of word i / 4) as the
+// exact bf16 pairs (v_i, v_{i+4}), i = 0..3: v_perm gathers bytes
+// (c0, c4, c1, c5) and (c2, c6, c3, c7), and each 16-bit half converts to a
+// bf16 pair (scale 1: the e8m0 scale multiplies the group's dot product).
+__device__ __forceinline__ bf16x8_t e4m3_chunk_to_bf16x8(const uint32_t (&f)[2]) {
+  const uint32_t a = __builtin_amdgcn_perm(f[1], f[0], 0x05010400u);
+  const uint32_t b = __builtin_amdgcn_perm(f[1], f[0], 0x07030602u);
+  const u32x4_t r{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a, 1.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, true))};
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
 #ifndef QSMOE_MXFP4_W
 #define QSMOE_MXFP4_W 1
@@ -704,8 +718,11 @@ constexpr int aff_min_wg() {
   return (QSMOE_AFF_MINWG3_G64 && !GATEUP && BITS == 4 && G == 64 && MT == 16) ? 3 : QSMOE_AFF_MINWG;
 }
 
-template <bool GATEUP, int BITS, int G, int MT>
+// FMT 0: affine codes as above; FMT 2: MXFP8 (BITS 8, G 32), E4M3 codes with
+// one e8m0 scale per group and no bias, so no X term.
+template <bool GATEUP, int BITS, int G, int MT, int FMT = 0>
 __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mfma_affine(MfmaArgs a) {
+  static_assert(FMT == 0 || (FMT == 2 && BITS == 8 && G == 32), "MXFP8 is 8-bit codes in groups of 32");
   constexpr int RB = kAffRB;
   constexpr int HB = GATEUP ? RB / 2 : RB;           // row blocks per matrix per wave
   constexpr int NTILE = 4 * HB * 16;                 // rows per matrix per workgroup
@@ -785,8 +802,11 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
   const char* cb1 = reinterpret_cast<const char*>(w1.codes) + static_cast<size_t>(rbase0) * row_bytes;
   const uint16_t* s0p = static_cast<const uint16_t*>(w0.scales) + static_cast<size_t>(rbase0) * rg;
   const uint16_t* s1p = static_cast<const uint16_t*>(w1.scales) + static_cast<size_t>(rbase0) * rg;
-  const uint16_t* b0p = w0.biases + static_cast<size_t>(rbase0) * rg;
-  const uint16_t* b1p = w1.biases + static_cast<size_t>(rbase0) * rg;
+  const uint16_t* b0p = FMT == 0 ? w0.biases + static_cast<size_t>(rbase0) * rg : nullptr;
+  const uint16_t* b1p = FMT == 0 ? w1.biases + static_cast<size_t>(rbase0) * rg : nullptr;
+  // MXFP8: one e8m0 byte per group, so a step's 4 groups are one word
+  const uint8_t* e0p = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(rbase0) * rg;
+  const uint8_t* e1p = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(rbase0) * rg;
   const uint32_t lrow_off = static_cast<uint32_t>(lrow * row_bytes), sc_off = static_cast<uint32_t>(r16 * rg);
   const int nsteps = cols / kKT;
   // this workgroup's K steps [ks_begin, ks_end) (the host makes slices a
@@ -867,6 +887,11 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
     const int kq = min(ks0 + g, nsteps - 1) * GPS;  // first group of that step
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (FMT == 2) {
+        const uint8_t* ep = (rb >= HB ? e1p : e0p) + static_cast<size_t>(16 * (rb % HB)) * rg + (sc_off + kq);
+        sc.s[rb][0] = *reinterpret_cast<const uint32_t*>(ep);
+        continue;
+      }
       const uint16_t* sp = (rb >= HB ? s1p : s0p) + static_cast<size_t>(16 * (rb % HB)) * rg + (sc_off + kq);
       const uint16_t* bp = (rb >= HB ? b1p : b0p) + static_cast<size_t>(16 * (rb % HB)) * rg + (sc_off + kq);
       if constexpr (GPS == 1) {
@@ -926,7 +951,7 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
 #pragma unroll
         for (int w = 0; w < SWS; ++w) {
           sw[rb][w] = __shfl(sc_cur.s[rb][w], (J & 3) * 16 + r16);
-          bw[rb][w] = __shfl(sc_cur.b[rb][w], (J & 3) * 16 + r16);
+          bw[rb][w] = FMT == 0 ? __shfl(sc_cur.b[rb][w], (J & 3) * 16 + r16) : 0u;
         }
 
       // group j's scale and bias applied to its partial tiles: after all
@@ -938,6 +963,14 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
       auto epilogue = [&](int j) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
+          if constexpr (FMT == 2) {
+            const float sc = e8m0_to_f32((sw[rb][0] >> (8 * j)) & 0xffu);
+#pragma unroll
+            for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[mb][rb][i] = fmaf(sc, dg[j][mb][rb][i], acc[mb][rb][i]);
+            continue;
+          }
           const float sc = f16_to_f32(static_cast<uint16_t>(sw[rb][j / 2] >> (16 * (j & 1))));
           const float bc = fmaf(-kOff, sc, f16_to_f32(static_cast<uint16_t>(bw[rb][j / 2] >> (16 * (j & 1)))));
 #pragma unroll
@@ -956,13 +989,19 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb)
             af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][mb * 16 + r16][32 * s + 8 * g]);
+          if constexpr (FMT == 0) {
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb)
-            xg[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                af[mb], ones, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : xg[j][mb], 0, 0, 0);
+            for (int mb = 0; mb < NMB; ++mb)
+              xg[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  af[mb], ones, pp == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : xg[j][mb], 0, 0, 0);
+          }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
-            const bf16x8_t bf = chunk_to_bf16x8<BITS>(qw[rb][s]);
+            bf16x8_t bf;
+            if constexpr (FMT == 2)
+              bf = e4m3_chunk_to_bf16x8(qw[rb][s]);
+            else
+              bf = chunk_to_bf16x8<BITS>(qw[rb][s]);
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
               dg[j][mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1074,6 +1113,7 @@ bool mfma_supported(const QMat& m, bool gateup, int64_t T, int k) {
   // activation rows are addressed with 32-bit element offsets
   if (T * k * m.cols >= (int64_t{1} << 31) || m.cols % kKT != 0) return false;
   if (m.fmt == 1) return m.bits == 4 && m.group == 32 && m.rows % (gateup ? 64 : 128) == 0;
+  if (m.fmt == 2) return m.bits == 8 && m.group == 32 && m.rows % ((gateup ? 32 : 64) * kAffRB) == 0;
   return affine_mfma_ok(m) && m.rows % ((gateup ? 32 : 64) * kAffRB) == 0;
 }
 
@@ -1134,6 +1174,12 @@ static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
       QSMOE_LAUNCH((k_mfma_mxfp4<GATEUP, 128, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NT2, 128)),
                          dim3(256), 0, s, a);
     }
+  } else if (m.fmt == 2) {
+    // MXFP8: the 8-bit affine layout with E4M3 decode and e8m0 group scales
+    constexpr int NTILE = (GATEUP ? 32 : 64) * kAffRB;
+    const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
+    QSMOE_LAUNCH((k_mfma_affine<GATEUP, 8, 32, 16, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, 16, a.ksplit)),
+                 dim3(256), lds, s, a);
   } else if (m.bits == 2) {
     launch_affine<GATEUP, 2, 16>(a, s);
   } else if (m.bits == 3) {

@@ -41,6 +41,8 @@ moe_status check_qtensor(const moe_qtensor& q, int experts, int rows, int cols) 
     if (!aligned(q.scales, 2) || !aligned(q.biases, 2)) return MOE_ERR_ALIGNMENT;
   } else if (q.format == MOE_FMT_MXFP4) {
     if (q.bits != 4 || q.group_size != 32) return MOE_ERR_UNSUPPORTED;
+  } else if (q.format == MOE_FMT_MXFP8) {
+    if (q.bits != 8 || q.group_size != 32) return MOE_ERR_UNSUPPORTED;
   } else {
     return MOE_ERR_UNSUPPORTED;
   }

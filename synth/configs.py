@@ -1,4 +1,4 @@
-"""The five synthetic MoE-layer workloads and their small variants.
+"""The synthetic MoE-layer workloads and their small variants.
 
 Shapes follow DeepSeek-V4-Flash as the pages pin them: hidden d=4096, expert
 intermediate I=2048, E=256 routed experts, top-6 routing (the hash table is
@@ -26,9 +26,10 @@ from typing import Optional
 class FormatSpec:
     """How one stacked projection is quantised.
 
-    fmt   -- "affine" (w = scale*q + bias, unsigned b-bit codes) or "mxfp4"
-             (e2m1 nibbles with one e8m0 exponent byte per 32 values)
-    bits  -- code width: 2, 3, 4 or 8 for affine; 4 for mxfp4
+    fmt   -- "affine" (w = scale*q + bias, unsigned b-bit codes), "mxfp4"
+             (e2m1 nibbles with one e8m0 exponent byte per 32 values) or
+             "mxfp8" (e4m3 bytes with one e8m0 exponent byte per 32 values)
+    bits  -- code width: 2, 3, 4 or 8 for affine; 4 for mxfp4; 8 for mxfp8
     group -- values sharing one scale(/bias) along the input dimension
     """
 
@@ -42,6 +43,8 @@ class FormatSpec:
             assert self.group in (32, 64, 128), self.group
         elif self.fmt == "mxfp4":
             assert self.bits == 4 and self.group == 32
+        elif self.fmt == "mxfp8":
+            assert self.bits == 8 and self.group == 32
         else:
             raise ValueError(self.fmt)
 
@@ -51,6 +54,7 @@ AFF8_G64 = FormatSpec("affine", 8, 64)
 AFF2_G128 = FormatSpec("affine", 2, 128)
 AFF3_G128 = FormatSpec("affine", 3, 128)
 MXFP4 = FormatSpec("mxfp4", 4, 32)
+MXFP8 = FormatSpec("mxfp8", 8, 32)
 
 
 @dataclass(frozen=True)
@@ -116,6 +120,9 @@ CONFIGS = {
     # Mixed low-bit decode batch: gate/up 2-bit g128, down 3-bit g128, shared 8-bit g64.
     "mixed": MoeConfig("mixed", 5, T=64, d=4096, I=2048, E=256, top_k=6, route="topk",
                        gate_up=AFF2_G128, down=AFF3_G128, shared=AFF8_G64, I_shared=2048),
+    # MXFP8 experts (e4m3 + e8m0 per 32), T=512 tokens, top-6 routing.
+    "mxfp8": MoeConfig("mxfp8", 6, T=512, d=4096, I=2048, E=256, top_k=6, route="topk",
+                       gate_up=MXFP8, down=MXFP8),
 }
 
 

@@ -19,13 +19,14 @@ this is exactly "codes uniform over [0, 2^b)". Affine scales are
 U(0.001, 0.01) * 16 / 2^b rounded to fp16 and biases are -2^(b-1) * scale, so
 every affine format spans the same +-8*U(0.001, 0.01) weight range (for b=4
 this is scale U(0.001, 0.01), bias -8*scale). e8m0 bytes are uniform over
-118..124.
+118..124 (mxfp4) or 110..116 (mxfp8, whose codes reach 448). mxfp8 code bytes
+are uniform over the 254 finite e4m3 codes (0x7F and 0xFF are NaN).
 
 Layouts (row-major, rows = output features, cols = input features, codes
 packed along cols as one LSB-first bit stream of little-endian uint32 words):
   codes  uint32  [n][rows][cols*bits/32]
-  scales fp16    [n][rows][cols/group]   (affine)   | uint8 e8m0 [n][rows][cols/32] (mxfp4)
-  biases fp16    [n][rows][cols/group]   (affine)   | None                          (mxfp4)
+  scales fp16    [n][rows][cols/group]   (affine)   | uint8 e8m0 [n][rows][cols/32] (mxfp4, mxfp8)
+  biases fp16    [n][rows][cols/group]   (affine)   | None                          (mxfp4, mxfp8)
 """
 from __future__ import annotations
 
@@ -121,6 +122,12 @@ def _empty_qtensor(spec: FormatSpec, rows: int, cols: int, n: int) -> QTensor:
 def _fill(q: QTensor, i: int, rng: np.random.Generator) -> None:
     rows, w = q.codes.shape[1], q.codes.shape[2]
     ng = q.scales.shape[2]
+    if q.spec.fmt == "mxfp8":
+        b = rng.integers(0, 254, size=(rows, 4 * w), dtype=np.uint16)
+        b = (b + (b >= 0x7F)).astype(np.uint8)
+        q.codes[i] = np.ascontiguousarray(b).view("<u4")
+        q.scales[i] = rng.integers(110, 117, size=(rows, ng), dtype=np.uint8)
+        return
     q.codes[i] = rng.integers(0, 2 ** 32, size=(rows, w), dtype=np.uint32)
     if q.spec.fmt == "affine":
         b = q.spec.bits

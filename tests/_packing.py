@@ -46,6 +46,27 @@ def make_mxfp4(codes_list, scale_bytes_list):
                    np.stack([np.asarray(s, dtype=np.uint8) for s in scale_bytes_list]), None)
 
 
+def make_mxfp8(codes_list, scale_bytes_list):
+    spec = FormatSpec("mxfp8", 8, 32)
+    codes = np.stack([pack_codes(c, 8) for c in codes_list])
+    rows, cols = np.asarray(codes_list[0]).shape
+    return QTensor(spec, rows, cols, codes,
+                   np.stack([np.asarray(s, dtype=np.uint8) for s in scale_bytes_list]), None)
+
+
+def e4m3_table_torch():
+    """The 256 e4m3 code values through torch's float8_e4m3fn conversion (an
+    implementation independent of the oracle's decoder)."""
+    import torch
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def finite_e4m3_codes(rng, shape):
+    """Uniform over the 254 non-NaN e4m3 codes (0x7F and 0xFF are NaN)."""
+    b = rng.integers(0, 254, size=shape)
+    return b + (b >= 0x7F)
+
+
 def bf16_round_exact(v: float) -> float:
     """Nearest bf16 (ties to even) of a finite normal-range double, via exact rationals."""
     if v == 0.0 or not math.isfinite(v):

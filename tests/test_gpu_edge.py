@@ -185,6 +185,10 @@ def test_deterministic_with_poisoned_workspace():
      ["router_hash", "permute", "routed_gateup", "routed_down", "combine"]),
     (variant("prefill", "disp_mxfp4", 217, T=64, d=512, I=256, E=8, top_k=2, bias_kind="normal"),
      ["router_logits", "router_topk", "permute", "routed_gateup_mfma", "routed_down_mfma", "combine"]),
+    (variant("mxfp8", "disp_mxfp8_mfma", 222, T=40, d=512, I=256, E=8, top_k=2),
+     ["router_logits", "router_topk", "permute", "routed_gateup_mfma", "routed_down_mfma", "combine"]),
+    (variant("mxfp8", "disp_mxfp8_gemv", 223, T=6, d=512, I=256, E=32, top_k=4),
+     ["router_logits", "router_topk", "permute", "routed_gateup", "routed_down", "combine"]),
 ], ids=lambda v: v.name if hasattr(v, "name") else "")
 def test_dispatch_picks_expected_kernels(cfg, expect):
     """Which kernels a step runs: the fused path for up to 4 top-k tokens; the

@@ -86,3 +86,9 @@ def test_prefill_mxfp4_full(full):
     cfg, layer, dl, ec = full("prefill")
     worst = _check(cfg, layer, dl, ec, synth.gen_x(cfg, 0), None, [0, 4095])
     print(f"prefill: max rel err {worst:.2e}")
+
+
+def test_mxfp8_full(full):
+    cfg, layer, dl, ec = full("mxfp8")
+    worst = _check(cfg, layer, dl, ec, synth.gen_x(cfg, 0), None, [0, 511])
+    print(f"mxfp8: max rel err {worst:.2e}")

@@ -65,6 +65,15 @@ SMALL = [
     variant("decode", "fused_k8_e40", 123, T=1, d=512, I=384, E=40, top_k=8, I_shared=128),
     # 2- and 3-bit codes on the streaming GEMV (under one token per expert)
     variant("mixed", "mixed_gemv", 117, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
+    # MXFP8 (e4m3 + e8m0 per 32): matrix cores (10 tokens per expert), the
+    # streaming GEMV (under one per expert), the fused single-token path with
+    # an 8-bit shared expert, and MXFP8 as the shared expert (matrix cores)
+    variant("mxfp8", "mxfp8_mfma", 126, T=40, d=512, I=256, E=8, top_k=2, bias_kind="normal"),
+    variant("mxfp8", "mxfp8_gemv", 127, T=6, d=768, I=256, E=32, top_k=4),
+    variant("mxfp8", "mxfp8_fused", 128, T=1, d=1024, I=256, E=16, top_k=4, shared=synth.configs.AFF8_G64,
+            I_shared=256),
+    variant("mxfp8", "mxfp8_shared", 129, T=16, d=512, I=256, E=8, top_k=2, shared=synth.configs.MXFP8,
+            I_shared=256),
 ]
 
 
@@ -106,12 +115,13 @@ def test_small_layer_parity(cfg):
     print(f"{cfg.name}: max rel err {worst:.2e}")
 
 
-@pytest.mark.parametrize("T,d,E", [(300, 1024, 64), (100, 1056, 40), (17, 4096, 256)])
+@pytest.mark.parametrize("T,d,E", [(600, 1024, 64), (300, 1024, 64), (100, 1056, 40), (17, 4096, 256)])
 def test_router_logits_and_topk_on_gpu_keys(T, d, E):
     """Logits within fp32 accumulation error of float64; the GPU top-k equals
     a host top-k over the GPU's own fp32 logits (scores in fp32), except where
-    two fp32 keys lie within a few ulps. Shapes: the 64-token tile kernel; the
-    K-split kernel with ragged tokens, experts and K steps; its full width."""
+    two fp32 keys lie within a few ulps. Shapes: the 64-token tile kernel
+    (over 512 tokens); the K-split kernel with ragged tokens, experts and K
+    steps; its full width."""
     cfg = variant("prefill", "logits", 111, T=T, d=d, I=128, E=E)
     wr, bias = synth.gen_router(cfg)
     layer = synth.Layer(cfg, wr, bias, None, synth.gen_routed_stacked(cfg), None)

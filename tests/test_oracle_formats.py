@@ -8,7 +8,8 @@ import pytest
 import torch
 
 import oracle
-from tests._packing import bf16_round_exact, make_affine, make_mxfp4, pack_codes
+from tests._packing import (bf16_round_exact, e4m3_table_torch, finite_e4m3_codes, make_affine, make_mxfp4,
+                            make_mxfp8, pack_codes)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -51,6 +52,66 @@ def check_e8m0_exhaustive():
 
 def test_e8m0_exhaustive():
     check_e8m0_exhaustive()
+
+
+# --------------------------------------------------------------------------- e4m3
+
+def check_e4m3_table():
+    """All 256 codes against torch's float8_e4m3fn (the OCP E4M3 format), NaN
+    codes included, and the format's closed-form landmarks."""
+    got = oracle.e4m3_decode(np.arange(256))
+    want = e4m3_table_torch()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))   # 0x80 is -0
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0                 # largest magnitude
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6           # smallest subnormal / normal
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def test_e4m3_table():
+    check_e4m3_table()
+
+
+def test_e4m3_times_e8m0_is_exact_in_bf16():
+    """Every finite e4m3 value times 2^(s - 127) over the synthetic scale bytes
+    is a bf16 value (3 mantissa bits fit in bf16's 7), so the kernels may
+    dequantise to bf16 without rounding."""
+    v = oracle.e4m3_decode(np.arange(256))
+    v = v[~np.isnan(v)][:, None] * oracle.e8m0_decode(np.arange(108, 122))[None, :]
+    t = torch.tensor(v, dtype=torch.float64)
+    assert torch.equal(t.to(torch.bfloat16).to(torch.float64), t)
+
+
+def check_mxfp8_rule():
+    rng = np.random.default_rng(45)
+    rows, cols = 2, 64
+    codes = finite_e4m3_codes(rng, (rows, cols))
+    sb = rng.integers(108, 122, size=(rows, cols // 32))
+    q = make_mxfp8([codes], [sb])
+    table = e4m3_table_torch()
+    got = oracle.dequant(q, 0)
+    for r in range(rows):
+        for c in range(cols):
+            assert got[r, c] == table[codes[r, c]] * 2.0 ** (int(sb[r, c // 32]) - 127)
+
+
+def test_mxfp8_rule():
+    check_mxfp8_rule()
+
+
+def test_mxfp8_byte_order():
+    """Byte j of a row (little-endian words) holds element j; the scale byte of
+    inputs 32..63 is the row's second one."""
+    q = make_mxfp8([np.zeros((1, 64), np.int64)], [np.array([[127, 128]])])
+    q.codes[0] = np.zeros((1, 16), np.uint32)
+    q.codes[0, 0, 0] = 0x0000B838        # element 0 = 1.0, element 1 = -1.0
+    q.codes[0, 0, 8] = 0x7E000000        # element 35 = 448
+    w = oracle.dequant(q, 0)[0]
+    assert w[0] == 1.0 and w[1] == -1.0 and w[35] == 896.0
+    assert np.count_nonzero(w) == 3
 
 
 # --------------------------------------------------------------------------- bit unpacking

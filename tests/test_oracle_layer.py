@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from synth import ExpertWeights, FormatSpec, MoeConfig, f32_to_bf16_bits
-from tests._packing import bf16_round_exact, make_affine, make_mxfp4
+from tests._packing import bf16_round_exact, e4m3_table_torch, finite_e4m3_codes, make_affine, make_mxfp4, make_mxfp8
 
 
 # --------------------------------------------------------------------------- permutation
@@ -58,6 +58,13 @@ def build_tiny_layer(seed, E=4, d=64, I=32, k=2, fmt="affine", bits=4, group=32,
             q = make_affine([codes], [s], [b], bits_, group_)
             W = [[float(s[r, c // group_]) * int(codes[r, c]) + float(b[r, c // group_]) for c in range(cols)]
                  for r in range(rows)]
+        elif fmt_ == "mxfp8":
+            codes = finite_e4m3_codes(rng, (rows, cols))
+            sb = rng.integers(110, 116, size=(rows, cols // 32))
+            q = make_mxfp8([codes], [sb])
+            tab8 = e4m3_table_torch()
+            W = [[float(tab8[codes[r, c]]) * 2.0 ** (int(sb[r, c // 32]) - 127) for c in range(cols)]
+                 for r in range(rows)]
         else:
             codes = rng.integers(0, 16, size=(rows, cols))
             sb = rng.integers(118, 125, size=(rows, cols // 32))
@@ -86,7 +93,7 @@ def build_tiny_layer(seed, E=4, d=64, I=32, k=2, fmt="affine", bits=4, group=32,
     if zero_router:
         wr[:] = 0
         bias[:] = 0
-    fs = FormatSpec(fmt, bits if fmt == "affine" else 4, group if fmt == "affine" else 32)
+    fs = FormatSpec(fmt, bits if fmt == "affine" else (8 if fmt == "mxfp8" else 4), group if fmt == "affine" else 32)
     cfg = MoeConfig("t", seed, T=1, d=d, I=I, E=E, top_k=k, route=route, gate_up=fs, down=fs,
                     shared=None if shared is None else FormatSpec("affine", shared, 32),
                     I_shared=I if shared is not None else 0, vocab=vocab,
@@ -143,7 +150,7 @@ def _x(seed, T, d, scale=1.0):
 
 
 @pytest.mark.parametrize("fmt,bits,shared", [("affine", 4, None), ("affine", 2, 8), ("affine", 3, None),
-                                             ("affine", 8, 4), ("mxfp4", 4, None)])
+                                             ("affine", 8, 4), ("mxfp4", 4, None), ("mxfp8", 8, None)])
 def test_tiny_layer_bruteforce(fmt, bits, shared):
     group = 32
     layer, plain = build_tiny_layer(100 + bits, fmt=fmt, bits=bits, group=group, shared=shared)

@@ -39,6 +39,19 @@ def m_e2m1_sign_bit(n):
     return orig["e2m1_decode"](np.asarray(n).astype(np.int64) ^ 0x8)
 
 
+def m_e4m3_bias_8(n):
+    """e4m3 decoded with exponent bias 8 (the FNUZ variant's bias)."""
+    return orig["e4m3_decode"](n) * 0.5
+
+
+def _tiny_bruteforce_mxfp8():
+    layer, plain = L.build_tiny_layer(106, fmt="mxfp8")
+    x = L._x(6, 2, layer.cfg.d)
+    ref = oracle.forward(layer, x)
+    for t, (ids, w, y) in enumerate(L.brute_layer(layer, plain, x)):
+        assert np.allclose(ref.y[t], y, rtol=1e-9, atol=1e-12 * max(abs(v) for v in y))
+
+
 def m_e8m0_off_by_one(b):
     return orig["e8m0_decode"](np.asarray(b).astype(np.int64) - 1)
 
@@ -115,6 +128,7 @@ def m_hash_sorted_ids(x64, wr, tid2eid, token_ids, routed_scale=1.0):
 MUTATIONS = [
     ("e2m1_decode", m_e2m1_sign_bit, [F.check_e2m1_table, F.check_mxfp4_rule]),
     ("e8m0_decode", m_e8m0_off_by_one, [F.check_e8m0_exhaustive, F.check_mxfp4_rule]),
+    ("e4m3_decode", m_e4m3_bias_8, [F.check_e4m3_table, F.check_mxfp8_rule, _tiny_bruteforce_mxfp8]),
     ("unpack_codes", m_unpack_msb_first, [F.check_unpack_known_words]),
     ("dequant", m_dequant_no_bias, [lambda: F.check_affine_rule(4, 64), L.check_zero_weights_give_zero]),
     ("dequant", m_mxfp4_scale_halved, [F.check_mxfp4_rule, _tiny_bruteforce_mxfp4]),
