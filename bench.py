@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=16)
-    p.add_argument("--workload", default="decode", choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8"])
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8", "stack43"])
     p.add_argument("--copies", type=int, default=0, help="device copies of the layer to rotate over (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
@@ -187,6 +188,140 @@ def cpu_baseline(cfg, layer, xs, toks, target_s):
             "sample": sample, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def main_stack(args):
+    """One decode token through the 43 MoE layers of the model (each layer with
+    its own experts, formats and expert count, and its own seeded activations:
+    attention and the residual stream between the layers are not part of the
+    layer). A step is the 43 layers in order on one stream, captured once as a
+    HIP graph."""
+    import numpy as np
+    import torch
+    import quantized_sparse_moe_amd as qm
+    import synth
+
+    qm.load()
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfgs = synth.stack_configs(T=1, steps=16)
+    T, L = 1, len(cfgs)
+    t_gen = time.perf_counter()
+    dls, xs, toks, touched, host_layers = [], [], [], [], []
+    for l, cfg in enumerate(cfgs):
+        layer = synth.gen_layer(cfg)
+        dls.append(qm.DeviceLayer.from_host(layer, dev))
+        host_layers.append(layer if l in (0, 3, L - 1) else None)   # kept for the CPU baseline sample
+        xs.append([torch.from_numpy(synth.gen_x(cfg, s).view(np.int16)).to(dev) for s in range(cfg.steps)])
+        tk = [synth.gen_token_ids(cfg, s) for s in range(cfg.steps)] if cfg.route == "hash" else None
+        toks.append([torch.from_numpy(t).to(dev) for t in tk] if tk else [None] * cfg.steps)
+        del layer
+        print(f"stack43: layer {l} built ({time.perf_counter() - t_gen:.0f} s)", file=sys.stderr, flush=True)
+    ws = max((dl.workspace(T) for dl in dls), key=lambda w: w.numel())
+    out = torch.empty((T, cfgs[0].d), dtype=torch.bfloat16, device=dev)
+    for l, cfg in enumerate(cfgs):
+        n = []
+        for i in range(cfg.steps):
+            ids, _ = qm.route(dls[l], xs[l][i], toks[l][i], ws)
+            n.append(int(torch.unique(ids).numel()))
+        touched.append(float(np.mean(n)))
+    gen_s = time.perf_counter() - t_gen
+
+    def step(i):
+        for l in range(L):
+            j = i % cfgs[l].steps
+            qm.forward(dls[l], xs[l][j], toks[l][j], ws=ws, out=out)
+
+    K, W = args.steps, args.warmup
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    assert qm.device_error(ws) == 0
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            for i in range(K):
+                step(i)
+    torch.cuda.current_stream().wait_stream(s)
+    graph.replay()  # untimed
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    graph.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / K
+    assert qm.device_error(ws) == 0
+
+    # per-kernel durations (HIP events taken by the dispatch), summed per step
+    # over the layers; the dominant kernel's bytes and time are averaged over
+    # its launches
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(32)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    per_launch, per_bytes = {}, {}
+    probe_steps = min(K, 4)
+    for i in range(probe_steps):
+        for l, cfg in enumerate(cfgs):
+            j = i % cfg.steps
+            names = qm.forward_probed(dls[l], xs[l][j], toks[l][j], out, ws, evs)
+            torch.cuda.synchronize()
+            for q, n in enumerate(names):
+                per_launch.setdefault(n, []).append(evs[2 * q].elapsed_time(evs[2 * q + 1]) * 1e3)
+                per_bytes.setdefault(n, []).append(kernel_bytes(n, cfg, dls[l], T, touched[l]))
+    step_us = {n: float(np.sum(v)) / probe_steps for n, v in per_launch.items()}
+    dom = max(step_us, key=step_us.get)
+    dom_us, dom_bytes = float(np.mean(per_launch[dom])), float(np.mean(per_bytes[dom]))
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload, dom),
+            "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": dom_us,
+            "launches_per_step": len(per_launch[dom]) // probe_steps}
+    sbytes = sum(step_bytes(cfg, dls[l], T, touched[l]) for l, cfg in enumerate(cfgs))
+    rec = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"stack43: one decode token through 43 MoE layers, d=4096, I=2048, top-6; layers "
+                                f"0-2 tid2eid hash over 256 experts, layers 3-42 top-6 over the 192 REAP25 "
+                                f"survivors; routed gate/up affine 2-bit g128 and down 3-bit g128 in layers 0-38, "
+                                f"affine 4-bit g64 in 39-42; shared expert I=2048 affine 8-bit g64 in every layer; "
+                                f"each layer reads its own seeded activations (16 batches)"),
+                   "tokens_per_step": T, "layers": L, "timing": "hipgraph",
+                   "touched_experts_per_layer": float(np.mean(touched))},
+        "hbm_gbps": sbytes / (ms * 1e-3) / 1e9,
+        "step_algorithmic_bytes": sbytes,
+        "roofline": roof,
+        "kernels_us": step_us,
+        "wall_s": wall,
+        "setup_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on one token through a sample of the layers (a hash layer,
+        # a pruned 2/3-bit layer, a 4-bit layer), scaled to the 43 layers
+        import oracle
+        smp = [l for l in range(L) if host_layers[l] is not None]
+        t0 = time.perf_counter()
+        for l in smp:
+            oracle.forward(host_layers[l], synth.gen_x(cfgs[l], 0),
+                           token_ids=synth.gen_token_ids(cfgs[l], 0) if cfgs[l].route == "hash" else None)
+        el = time.perf_counter() - t0
+        per_layer = el / len(smp)
+        rec["cpu_baseline"] = {"value": 1.0 / (per_layer * L), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"one token through layers {smp} ({el:.1f} s), scaled to {L} layers",
+                               "host_cpus": len(os.sched_getaffinity(0))}
+        try:
+            from threadpoolctl import threadpool_info
+            rec["cpu_baseline"]["cores"] = int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+        except Exception:  # pragma: no cover
+            pass
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -204,6 +339,10 @@ def main():
             torch.mul(src, 1.0, out=dst)  # reads n bytes, writes n bytes
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 3}))
+        return
+
+    if args.workload == "stack43":
+        main_stack(args)
         return
 
     import quantized_sparse_moe_amd as qm

@@ -12,6 +12,7 @@ from .configs import (  # noqa: F401
     CONFIGS,
     config,
     variant,
+    stack_configs,
 )
 from .gen import (  # noqa: F401
     QTensor,

@@ -130,6 +130,35 @@ def config(name: str) -> MoeConfig:
     return CONFIGS[name]
 
 
+# The 43 MoE layers of one decode token through the whole model.
+#  * precision per layer from the "DeepSeek-V4-Flash-0731-MLX-Serve-mixed-2-3-8bit"
+#    precision table: routed gate/up affine 2-bit g128 and down 3-bit g128 in
+#    layers 0-38, affine 4-bit g64 in layers 39-42; shared experts 8-bit g64;
+#  * expert counts from the "REAP-pruned builds" section of the alphaneural
+#    card "DeepSeek-V4-Flash-MLX-4bit": layers 0-2 route through the tid2eid
+#    table and keep all 256 experts; the other 40 keep the 192 survivors of
+#    REAP25, with the router rows of the survivors only (top-6 renormalised
+#    over them).
+STACK_LAYERS = 43
+STACK_HASH_LAYERS = 3
+STACK_4BIT_FROM = 39
+STACK_SURVIVORS = 192
+
+
+def stack_configs(T: int = 1, steps: int = 16) -> list:
+    """Per-layer configs of the 43-layer stack (seed 100 + layer)."""
+    out = []
+    for l in range(STACK_LAYERS):
+        hash_layer = l < STACK_HASH_LAYERS
+        fmt_gu, fmt_dn = (AFF4_G64, AFF4_G64) if l >= STACK_4BIT_FROM else (AFF2_G128, AFF3_G128)
+        out.append(MoeConfig(f"stack43_l{l}", 100 + l, T=T, d=4096, I=2048,
+                             E=256 if hash_layer else STACK_SURVIVORS, top_k=6,
+                             route="hash" if hash_layer else "topk", gate_up=fmt_gu, down=fmt_dn,
+                             shared=AFF8_G64, I_shared=2048, vocab=129280 if hash_layer else 0,
+                             bias_kind="none" if hash_layer else "normal", steps=steps))
+    return out
+
+
 def variant(base: MoeConfig | str, name: str, seed: int, **changes) -> MoeConfig:
     """A smaller or reshaped copy of a workload under its own seed."""
     if isinstance(base, str):

@@ -26,7 +26,10 @@ def full():
             cache.clear()
             gc.collect()
             torch.cuda.empty_cache()
-            cfg = synth.config(name)
+            if name.startswith("stack43_l"):
+                cfg = synth.stack_configs()[int(name[len("stack43_l"):])]
+            else:
+                cfg = synth.config(name)
             layer = synth.gen_layer(cfg)                 # stacked experts, uploaded once
             dl = qm.DeviceLayer.from_host(layer)
             layer.routed = None                          # oracle draws experts on demand
@@ -92,3 +95,15 @@ def test_mxfp8_full(full):
     cfg, layer, dl, ec = full("mxfp8")
     worst = _check(cfg, layer, dl, ec, synth.gen_x(cfg, 0), None, [0, 511])
     print(f"mxfp8: max rel err {worst:.2e}")
+
+
+@pytest.mark.parametrize("layer", [0, 3, 42])
+def test_stack43_layer_full(full, layer):
+    """Layers of the 43-layer stack at full size, one token: a hash layer over
+    256 experts, a REAP25-pruned 2/3-bit layer and a pruned 4-bit layer (each
+    with its 8-bit shared expert)."""
+    cfg, lyr, dl, ec = full(f"stack43_l{layer}")
+    hashed = cfg.route == "hash"
+    worst = max(_check(cfg, lyr, dl, ec, synth.gen_x(cfg, s), synth.gen_token_ids(cfg, s) if hashed else None, [0])
+                for s in (0, 1))
+    print(f"stack43 layer {layer}: max rel err {worst:.2e}")

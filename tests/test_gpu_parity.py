@@ -74,6 +74,13 @@ SMALL = [
             I_shared=256),
     variant("mxfp8", "mxfp8_shared", 129, T=16, d=512, I=256, E=8, top_k=2, shared=synth.configs.MXFP8,
             I_shared=256),
+    # layers of the 43-layer stack at small sizes: a REAP25-pruned layer (192
+    # experts) on the fused single-token path with 2/3-bit experts, and a
+    # hash-routed single-token layer with a shared expert
+    variant("mixed", "stack_pruned_fused", 130, T=1, d=1024, I=256, E=192, top_k=6, I_shared=256),
+    variant("hash", "stack_hash_shared", 131, T=1, d=1024, I=256, E=64, vocab=500,
+            gate_up=synth.configs.AFF2_G128, down=synth.configs.AFF3_G128, shared=synth.configs.AFF8_G64,
+            I_shared=256),
 ]
 
 

@@ -93,6 +93,27 @@ def test_bias_ranks_but_does_not_weight():
     assert w[0, 0] < w[0, 1]
 
 
+def test_pruned_router_equals_survivor_masked_router():
+    """REAP-pruned layers (alphaneural card "DeepSeek-V4-Flash-MLX-4bit",
+    section "REAP-pruned builds": the router renormalizes over survivors)
+    keep only the survivors' router rows. Routing over those rows, mapped
+    back through the survivor list, equals routing over all experts with the
+    dropped ones masked out (bias -inf): same ids in the same order, same
+    weights."""
+    rng = np.random.default_rng(31)
+    E, k, T = 256, 6, 50
+    survivors = np.sort(rng.choice(E, 192, replace=False))      # REAP25 keeps 192
+    logits = rng.standard_normal((T, E))
+    bias = rng.standard_normal(E) * 0.1
+    ids_p, w_p, _, _ = oracle.route_topk(logits[:, survivors], bias[survivors], k)
+    masked = np.full(E, -np.inf)
+    masked[survivors] = bias[survivors]
+    ids_m, w_m, _, _ = oracle.route_topk(logits, masked, k)
+    assert np.array_equal(survivors[ids_p], ids_m)
+    assert np.allclose(w_p, w_m, rtol=1e-15)
+    assert np.allclose(w_p.sum(1), 1.0, rtol=1e-14)
+
+
 def test_router_logits_loop():
     rng = np.random.default_rng(9)
     x = rng.standard_normal((3, 40))
