@@ -68,6 +68,34 @@ __global__ __launch_bounds__(256) void k_dec_router(DecodeArgs a) {
   QSMOE_TL(0, 7);
 }
 
+// Hash route of token t by one wave (the pages' tid2eid table, as k_hash):
+// lane j < k takes expert tid2eid[token][j]; the weights are the launch-1
+// scores of those experts renormalised over the k slots (summed in slot
+// order). A token id or table entry out of range sets the device error word
+// (publish: one workgroup only), the id becomes 0 and the token's weights 0.
+__device__ __forceinline__ void dec_hash_head(const DecodeArgs& a, int t, bool publish, int& id, float& wt) {
+  const int lane = lane_id();
+  int tok = a.token_ids[t];
+  bool ok = true;
+  if (tok < 0 || tok >= a.vocab) {
+    if (publish && lane == 0) set_device_error(a.err, 1);
+    tok = 0;
+    ok = false;
+  }
+  int e = lane < a.k ? a.tid2eid[static_cast<size_t>(tok) * a.k + lane] : 0;
+  const bool bad = lane < a.k && (e < 0 || e >= a.E);
+  if (__ballot(bad) != 0) {
+    if (publish && lane == 0) set_device_error(a.err, 2);
+    ok = false;
+  }
+  e = (bad || lane >= a.k) ? 0 : e;
+  const float s = lane < a.k ? a.scores[static_cast<size_t>(t) * a.E + e] : 0.0f;
+  float total = 0.0f;
+  for (int j = 0; j < a.k; ++j) total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
+  id = e;
+  wt = ok ? (total > 0.0f ? s / total : 1.0f / static_cast<float>(a.k)) * a.routed_scale : 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Launch 2. Every workgroup first selects each token's top-k from the
 // launch-1 keys (wave t: token t, keys in registers; same selection as
@@ -80,20 +108,24 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   QSMOE_TL(1, 0);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   if (wave < a.T) {
-    uint64_t key[4];
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      const bool ok = e < a.E;
-      const size_t o = static_cast<size_t>(wave) * a.E + (ok ? e : 0);
-      key[i] = a.keys[o];
-      sc[i] = a.scores[o];
-      key[i] = ok ? key[i] : 0;
-    }
     int id;
     float wt;
-    topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
+    if (a.hash) {
+      dec_hash_head(a, wave, blockIdx.x == 0, id, wt);
+    } else {
+      uint64_t key[4];
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        const bool ok = e < a.E;
+        const size_t o = static_cast<size_t>(wave) * a.E + (ok ? e : 0);
+        key[i] = a.keys[o];
+        sc[i] = a.scores[o];
+        key[i] = ok ? key[i] : 0;
+      }
+      topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
+    }
     if (lane < a.k) {
       s_ids[wave * a.k + lane] = id;
       if (blockIdx.x == 0) {
@@ -144,19 +176,23 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   QSMOE_TL(1, 0);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   if (wave == 0) {
-    uint64_t key[4];
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      const bool ok = e < a.E;
-      key[i] = a.keys[ok ? e : 0];
-      sc[i] = a.scores[ok ? e : 0];
-      key[i] = ok ? key[i] : 0;
-    }
     int id;
     float wt;
-    topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
+    if (a.hash) {
+      dec_hash_head(a, 0, blockIdx.x == 0, id, wt);
+    } else {
+      uint64_t key[4];
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        const bool ok = e < a.E;
+        key[i] = a.keys[ok ? e : 0];
+        sc[i] = a.scores[ok ? e : 0];
+        key[i] = ok ? key[i] : 0;
+      }
+      topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
+    }
     if (lane < a.k) {
       s_ids[lane] = id;
       if (blockIdx.x == 0) {

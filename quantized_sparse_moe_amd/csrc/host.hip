@@ -144,10 +144,13 @@ FwdLayout forward_layout(const moe_layer& L, int T) {
   o += align_up(tk * 4);
   f.w = o;
   o += align_up(tk * 4);
+  // logits: top-k routing, and hash routing on the small-batch path (whose
+  // launch 1 computes every expert's logit and score)
+  const bool small = T <= 4;
   f.logits = o;
-  o += L.router.mode == MOE_ROUTE_TOPK ? align_up(static_cast<size_t>(T) * E * 4) : 0;
+  o += L.router.mode == MOE_ROUTE_TOPK || small ? align_up(static_cast<size_t>(T) * E * 4) : 0;
   f.keys = o;  // small-batch path only (T <= 4): ranking keys and scores
-  o += L.router.mode == MOE_ROUTE_TOPK && T <= 4 ? align_up(static_cast<size_t>(T) * E * 12) : 0;
+  o += small ? align_up(static_cast<size_t>(T) * E * 12) : 0;
   f.offsets = o;
   o += align_up((E + 1) * 4);
   f.perm = o;
@@ -410,8 +413,13 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
   const FwdLayout f = forward_layout(L, T);
   if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
   const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;
-  if (L.router.mode == MOE_ROUTE_TOPK) {
+  if (L.router.mode == MOE_ROUTE_TOPK || L.router.mode == MOE_ROUTE_HASH) {
     DecodeArgs da{};
+    da.hash = L.router.mode == MOE_ROUTE_HASH;
+    da.token_ids = token_ids;
+    da.tid2eid = L.router.tid2eid;
+    da.vocab = L.router.vocab;
+    da.err = at<int32_t>(ws, 0);
     da.x = x_bf16;
     da.T = T;
     da.d = d;

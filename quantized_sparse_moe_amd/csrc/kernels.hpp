@@ -110,6 +110,11 @@ struct DecodeArgs {
   int32_t n_logit_blocks;  // workgroups of launch 1 that compute logits (set by its launcher)
   int32_t* ids;            // workspace int32 [T][k], written by launch 2
   float* w;                // workspace fp32 [T][k], written by launch 2
+  int32_t hash;            // tid2eid routing: ids from the table, weights from the launch-1 scores
+  const int32_t* token_ids;  // [T] (hash)
+  const int32_t* tid2eid;    // [vocab][k] (hash)
+  int32_t vocab;
+  int32_t* err;            // workspace error word
 };
 bool decode_path_supported(const DecodeArgs& a);
 hipError_t launch_dec_router(const DecodeArgs& a, hipStream_t s);

@@ -73,21 +73,23 @@ def test_zero_tokens_launches_nothing():
     assert st.out.shape == (0, cfg.d) and st.ids.shape == (0, cfg.top_k)
 
 
-def test_out_of_range_token_id_sets_error_word():
-    cfg = variant("hash", "badtok", 205, T=8, d=256, I=128, E=16, top_k=2, vocab=50)
+# T=8: the staged path (k_hash); T=3: the fused small-batch path
+@pytest.mark.parametrize("T,bad", [(8, 3), (3, 1)])
+def test_out_of_range_token_id_sets_error_word(T, bad):
+    cfg = variant("hash", "badtok", 205, T=T, d=256, I=128, E=16, top_k=2, vocab=50)
     layer = synth.gen_layer(cfg)
     dl = qm.DeviceLayer.from_host(layer)
     x = synth.gen_x(cfg, 0)
     tok = synth.gen_token_ids(cfg, 0)
     good = tok.copy()
-    tok[3] = 50
+    tok[bad] = 50
     ws = dl.workspace(cfg.T)
     out = qm.forward(dl, xdev(x), torch.from_numpy(tok).cuda(), out_dtype="f32", ws=ws)
     assert qm.device_error(ws) & _lib.MOE_DEVERR_TOKEN_ID
     ref = oracle.forward(layer, x, token_ids=good)
-    keep = [t for t in range(cfg.T) if t != 3]
+    keep = [t for t in range(cfg.T) if t != bad]
     assert rel_err(out.cpu().numpy()[keep], ref.y[keep]).max() <= TOL
-    assert torch.count_nonzero(out[3]).item() == 0
+    assert torch.count_nonzero(out[bad]).item() == 0
     qm.workspace_init(ws)
     assert qm.device_error(ws) == 0
 
@@ -183,6 +185,8 @@ def test_deterministic_with_poisoned_workspace():
       "combine"]),
     (variant("hash", "disp_hash_gemv", 216, T=40, d=512, I=256, E=64, vocab=1000),
      ["router_hash", "permute", "routed_gateup", "routed_down", "combine"]),
+    (variant("hash", "disp_hash_fused", 224, T=2, d=512, I=256, E=64, vocab=1000),
+     ["dec_router", "dec_gateup", "dec_down_combine"]),
     (variant("prefill", "disp_mxfp4", 217, T=64, d=512, I=256, E=8, top_k=2, bias_kind="normal"),
      ["router_logits", "router_topk", "permute", "routed_gateup_mfma", "routed_down_mfma", "combine"]),
     (variant("mxfp8", "disp_mxfp8_mfma", 222, T=40, d=512, I=256, E=8, top_k=2),
@@ -191,7 +195,8 @@ def test_deterministic_with_poisoned_workspace():
      ["router_logits", "router_topk", "permute", "routed_gateup", "routed_down", "combine"]),
 ], ids=lambda v: v.name if hasattr(v, "name") else "")
 def test_dispatch_picks_expected_kernels(cfg, expect):
-    """Which kernels a step runs: the fused path for up to 4 top-k tokens; the
+    """Which kernels a step runs: the fused path for up to 4 tokens (top-k or
+    hash routing); the
     streaming GEMV under one token per expert (2/3-bit) or four (4-bit); the
     matrix-core grouped GEMM above that; the shared expert on the matrix cores
     from 8 tokens, its K split over workgroups (with finishers) while its

@@ -78,6 +78,7 @@ SMALL = [
     # experts) on the fused single-token path with 2/3-bit experts, and a
     # hash-routed single-token layer with a shared expert
     variant("mixed", "stack_pruned_fused", 130, T=1, d=1024, I=256, E=192, top_k=6, I_shared=256),
+    variant("hash", "hash_fused_t3", 132, T=3, d=512, I=256, E=32, vocab=300),
     variant("hash", "stack_hash_shared", 131, T=1, d=1024, I=256, E=64, vocab=500,
             gate_up=synth.configs.AFF2_G128, down=synth.configs.AFF3_G128, shared=synth.configs.AFF8_G64,
             I_shared=256),
