@@ -79,6 +79,15 @@ SMALL = [
     # hash-routed single-token layer with a shared expert
     variant("mixed", "stack_pruned_fused", 130, T=1, d=1024, I=256, E=192, top_k=6, I_shared=256),
     variant("hash", "hash_fused_t3", 132, T=3, d=512, I=256, E=32, vocab=300),
+    # 2-bit rows whose lanes load two adjacent chunks at once (even chunk
+    # counts, 2 or 4 chunks per lane): fused single token at d=4096; GEMV with
+    # d=3072 and I=2560 (lanes past the row masked); odd chunk count (d=4064,
+    # groups of 32) keeps one chunk per load
+    variant("mixed", "aff2_paired_fused", 133, T=1, d=4096, I=256, E=16, top_k=4, I_shared=256),
+    variant("mixed", "aff2_paired_gemv", 134, T=6, d=3072, I=2560, E=64, top_k=4, shared=None,
+            down=synth.configs.AFF2_G128),
+    variant("mixed", "aff2_odd_chunks", 135, T=6, d=4064, I=256, E=64, top_k=4, shared=None,
+            gate_up=synth.configs.FormatSpec("affine", 2, 32), down=synth.configs.FormatSpec("affine", 2, 32)),
     variant("hash", "stack_hash_shared", 131, T=1, d=1024, I=256, E=64, vocab=500,
             gate_up=synth.configs.AFF2_G128, down=synth.configs.AFF3_G128, shared=synth.configs.AFF8_G64,
             I_shared=256),
