@@ -39,6 +39,7 @@ __all__ = [
     "bf16_bits_to_f64", "round_bf16", "e2m1_decode", "e4m3_decode", "e8m0_decode", "unpack_codes",
     "dequant", "sqrtsoftplus", "silu", "router_logits", "route_topk", "route_hash",
     "combine_weights_for_ids", "permute", "swiglu_expert", "forward", "forward_tokens",
+    "pack_codes", "quantize_affine",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -159,6 +160,47 @@ def dequant(q, e: int = 0) -> np.ndarray:
         scale = np.repeat(e8m0_decode(q.scales[e]), 32, axis=-1)
         return e4m3_decode(codes) * scale
     raise ValueError(spec.fmt)
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Inverse of unpack_codes: b-bit codes [..., cols] -> one LSB-first bit
+    stream over little-endian uint32 words [..., cols*b/32]."""
+    c = np.asarray(codes, dtype=np.int64)
+    lead, cols = c.shape[:-1], c.shape[-1]
+    assert (cols * bits) % 32 == 0 and c.min(initial=0) >= 0 and c.max(initial=0) < (1 << bits)
+    stream = np.zeros((*lead, cols, bits), dtype=np.uint8)
+    for i in range(bits):
+        stream[..., i] = (c >> i) & 1
+    stream = stream.reshape(*lead, cols * bits)
+    return np.packbits(stream, axis=-1, bitorder="little").view("<u4")
+
+
+def quantize_affine(w_bits, bits: int, group: int):
+    """Plain min/max affine quantisation of bf16 weights [rows][cols], the
+    conversion step before the layer ([CARD4] "Conversion": mlx_lm.convert
+    -q --q-bits 4 --q-group-size 64; [SERVE] contrasts its calibrated search
+    with plain min/max). READINGS (the pages give the recipe, not its
+    arithmetic): per group of ``group`` consecutive inputs of a row,
+        scale = fp16((max - min) / (2^b - 1)),  bias = fp16(min),
+        q = clamp(rint((w - bias) / scale), 0, 2^b - 1)   (q = 0 if scale == 0),
+    with fp16 round-to-nearest-even. The code is an integer that floating
+    point decides, so it is computed in fp32 (the kernel's precision) with
+    IEEE operations in this order: subtraction, division, rint (ties to even).
+    Returns (codes uint32 [rows][cols*b/32], scales fp16, biases fp16 [rows][cols/group]).
+    """
+    w = bf16_bits_to_f64(w_bits).astype(np.float32)
+    rows, cols = w.shape
+    assert cols % group == 0
+    g = w.reshape(rows, cols // group, group)
+    lo, hi = g.min(axis=-1), g.max(axis=-1)
+    levels = np.float32((1 << bits) - 1)
+    scale = ((hi - lo) / levels).astype(np.float16)
+    bias = lo.astype(np.float16)
+    s32, b32 = scale.astype(np.float32)[..., None], bias.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.rint((g - b32) / s32)
+    q = np.where(s32 == 0, 0.0, np.clip(t, 0, levels)).astype(np.int64).reshape(rows, cols)
+    return pack_codes(q, bits), scale, bias
 
 
 # ----------------------------------------------------------------------------

@@ -7,6 +7,7 @@ import oracle
 import oracle.moe as om
 from tests import test_oracle_formats as F
 from tests import test_oracle_layer as L
+from tests import test_oracle_quant as Q
 from tests import test_oracle_router as R
 
 
@@ -50,6 +51,28 @@ def _tiny_bruteforce_mxfp8():
     ref = oracle.forward(layer, x)
     for t, (ids, w, y) in enumerate(L.brute_layer(layer, plain, x)):
         assert np.allclose(ref.y[t], y, rtol=1e-9, atol=1e-12 * max(abs(v) for v in y))
+
+
+def m_quant_levels_pow2(w_bits, bits, group):
+    """Scale from 2^b steps instead of 2^b - 1."""
+    codes, scale, bias = orig["quantize_affine"](w_bits, bits + 0, group)
+    w = om.bf16_bits_to_f64(w_bits).astype(np.float32)
+    g = w.reshape(w.shape[0], -1, group)
+    scale = ((g.max(-1) - g.min(-1)) / np.float32(1 << bits)).astype(np.float16)
+    q = np.clip(np.rint((g - bias.astype(np.float32)[..., None]) / scale.astype(np.float32)[..., None]), 0,
+                (1 << bits) - 1).astype(np.int64).reshape(w.shape)
+    return om.pack_codes(q, bits), scale, bias
+
+
+def m_quant_truncate(w_bits, bits, group):
+    """Codes truncated instead of rounded to nearest."""
+    w = om.bf16_bits_to_f64(w_bits).astype(np.float32)
+    g = w.reshape(w.shape[0], -1, group)
+    scale = ((g.max(-1) - g.min(-1)) / np.float32((1 << bits) - 1)).astype(np.float16)
+    bias = g.min(-1).astype(np.float16)
+    q = np.clip(np.floor((g - bias.astype(np.float32)[..., None]) / scale.astype(np.float32)[..., None]), 0,
+                (1 << bits) - 1).astype(np.int64).reshape(w.shape)
+    return om.pack_codes(q, bits), scale, bias
 
 
 def m_e8m0_off_by_one(b):
@@ -140,6 +163,8 @@ MUTATIONS = [
     ("swiglu_expert", m_swiglu_transposed_down, [L.check_one_hot_extracts_column]),
     ("round_bf16", m_round_via_fp32, [F.check_bf16_rounding]),
     ("route_hash", m_hash_sorted_ids, [R.check_hash_route_lookup]),
+    ("quantize_affine", m_quant_levels_pow2, [Q.check_grid_roundtrip, Q.check_quant_bounds]),
+    ("quantize_affine", m_quant_truncate, [Q.check_quant_bounds]),
 ]
 
 
