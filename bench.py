@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8", "stack43"])
+                   choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8", "stack43", "quantize"])
     p.add_argument("--copies", type=int, default=0, help="device copies of the layer to rotate over (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
@@ -186,6 +186,69 @@ def cpu_baseline(cfg, layer, xs, toks, target_s):
               f"(each call dequantises its touched experts to float64), {el:.1f} s")
     return {"value": n_tok / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": sample, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main_quantize(args):
+    """The conversion step before the layer: plain min/max affine quantisation
+    (4-bit, groups of 64) of 128 experts' bf16 gate projections, [2048][4096]
+    each, stacked as one [262144][4096] matrix: one launch per step."""
+    import numpy as np
+    import torch
+    import quantized_sparse_moe_amd as qm
+    import synth
+
+    qm.load()
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    experts, rows, cols, bits, group = 128, 2048, 4096, 4, 64
+    t_gen = time.perf_counter()
+    w = torch.empty((experts * rows, cols), dtype=torch.int16, device=dev)
+    for e in range(experts):
+        w[e * rows:(e + 1) * rows] = torch.from_numpy(synth.gen_bf16_weights(21, e, rows, cols).view(np.int16)).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    gen_s = time.perf_counter() - t_gen
+    n = experts * rows * cols
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        qm.quantize_affine(w, bits, group, err=err)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(K):
+        qm.quantize_affine(w, bits, group, err=err)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / K
+    assert int(err.item()) == 0
+    nbytes = n * 2 + n * bits // 8 + (n // group) * 4   # bf16 in; codes, fp16 scale and bias out
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "affine quantiser weights/s (conversion step before the layer)", "value": n / (ms * 1e-3),
+        "unit": "weights/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"quantize: {experts} x [{rows}][{cols}] bf16 N(0, 0.02) weights -> affine "
+                               f"{bits}-bit g{group} (one launch)", "timing": "eager, one launch per step"},
+        "roofline": {"bound": "hbm", "kernel": "k_quantize_affine", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload,
+                                                                                                  "k_quantize_affine"),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": ms * 1e3},
+        "wall_s": wall, "setup_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            oracle.quantize_affine(synth.gen_bf16_weights(21, done, 256, cols), bits, group)
+            done += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done * 256 * cols / el, "unit": "weights/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{done} oracle calls on [256][{cols}] blocks ({el:.1f} s)",
+                               "host_cpus": len(os.sched_getaffinity(0))}
+    print(json.dumps(rec), flush=True)
 
 
 def main_stack(args):
@@ -343,6 +406,9 @@ def main():
 
     if args.workload == "stack43":
         main_stack(args)
+        return
+    if args.workload == "quantize":
+        main_quantize(args)
         return
 
     import quantized_sparse_moe_amd as qm

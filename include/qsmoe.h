@@ -66,6 +66,8 @@ typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out_dtype;
 #define MOE_DEVERR_TOKEN_ID 1  /* token id outside [0, vocab)                  */
 #define MOE_DEVERR_HASH_ID 2   /* tid2eid entry outside [0, E)                  */
 #define MOE_DEVERR_EXPERT_ID 4 /* top-k id passed to moe_permute outside [0, E) */
+#define MOE_DEVERR_QUANT_INPUT 8 /* moe_quantize_affine: a NaN/inf weight, or a group's
+                                    scale or bias beyond fp16 (outputs unspecified) */
 
 /*
  * One stacked quantised projection: num_experts matrices of [rows][cols].
@@ -236,6 +238,29 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
 
 /* Synchronises `stream`, then copies the workspace error word to *code_out. */
 moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream);
+
+/*
+ * Plain min/max affine quantisation of bf16 weights: the conversion step
+ * before the layer ([CARD4] "Conversion": mlx_lm.convert -q --q-bits b
+ * --q-group-size g; [SERVE] contrasts its calibrated search with plain
+ * min/max). Produces a MOE_FMT_AFFINE projection for one matrix (call per
+ * expert, or once on E stacked matrices as rows = E * rows). Per group of g
+ * inputs of a row, in fp32 with IEEE rounding (the pages give the recipe,
+ * not its arithmetic; this is the reading taken):
+ *     scale = fp16_rne((max - min) / (2^b - 1)),  bias = fp16_rne(min),
+ *     q = clamp(rint((w - bias) / scale), 0, 2^b - 1), q = 0 if scale == 0.
+ *   w_bf16 : device bf16 [rows][cols], 16-byte aligned
+ *   codes  : device uint32 [rows][cols * bits / 32], 16-byte aligned (written)
+ *   scales, biases : device fp16 [rows][cols / g], 2-byte aligned (written)
+ *   err    : device int32 or NULL; MOE_DEVERR_QUANT_INPUT is ORed in for a
+ *            NaN/inf weight or a group whose scale or bias overflows fp16.
+ * bits in {2, 3, 4, 8}, g in {32, 64, 128}, cols % g == 0, rows >= 0.
+ * Asynchronous on `stream`; allocates nothing. Errors: INVALID_ARG (null or
+ * negative), UNSUPPORTED (bits, g, cols), ALIGNMENT, HIP.
+ */
+moe_status moe_quantize_affine(const uint16_t* w_bf16, int64_t rows, int32_t cols, int32_t bits, int32_t group_size,
+                               uint32_t* codes, uint16_t* scales, uint16_t* biases, int32_t* err,
+                               hipStream_t stream);
 
 const char* moe_status_string(moe_status status);
 

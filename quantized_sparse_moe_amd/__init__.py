@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     forward_probed,
     forward_staged,
     permute,
+    quantize_affine,
     route,
     router_logits,
     workspace_init,

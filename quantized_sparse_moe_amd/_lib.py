@@ -7,7 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, Structure, c_char_p, c_float, c_int32, c_size_t, c_void_p
+from ctypes import c_int64, POINTER, Structure, c_char_p, c_float, c_int32, c_size_t, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsmoe.so")
 
@@ -29,6 +29,7 @@ MOE_OUT_F32 = 1
 MOE_DEVERR_TOKEN_ID = 1
 MOE_DEVERR_HASH_ID = 2
 MOE_DEVERR_EXPERT_ID = 4
+MOE_DEVERR_QUANT_INPUT = 8
 
 
 class QTensorC(Structure):
@@ -70,6 +71,8 @@ _SIGS = {
                                      POINTER(c_int32)]),
     "moe_router_logits": (c_int32, [POINTER(RouterC), c_void_p, c_int32, c_void_p, c_void_p]),
     "moe_device_error": (c_int32, [c_void_p, POINTER(c_int32), c_void_p]),
+    "moe_quantize_affine": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p]),
     "moe_status_string": (c_char_p, [c_int32]),
     "moe_version": (c_char_p, []),
 }

@@ -170,6 +170,20 @@ def route(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tensor]
     return ids, w
 
 
+def quantize_affine(w: torch.Tensor, bits: int, group: int, err: Optional[torch.Tensor] = None, stream=None):
+    """Plain min/max affine quantisation of bf16 weights [rows][cols] (moe_quantize_affine):
+    returns (codes uint32 [rows][cols*bits/32], scales fp16, biases fp16 [rows][cols/group])
+    as device tensors (the fp16 ones as int16 bit patterns)."""
+    w = _bits_tensor(w)
+    rows, cols = w.shape
+    codes = torch.empty((rows, cols * bits // 32), dtype=torch.int32, device=w.device)
+    scales = torch.empty((rows, cols // group), dtype=torch.int16, device=w.device)
+    biases = torch.empty_like(scales)
+    check(_lib.load().moe_quantize_affine(_ptr(w), rows, cols, bits, group, _ptr(codes), _ptr(scales), _ptr(biases),
+                                          None if err is None else _ptr(err), _stream(stream)), "moe_quantize_affine")
+    return codes, scales, biases
+
+
 def permute(ids: torch.Tensor, num_experts: int, ws: torch.Tensor, stream=None):
     T, k = ids.shape
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=ids.device)

@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["host.hip", "router.hip", "permute.hip", "ffn_gemv.hip", "ffn_mfma.hip", "decode.hip", "combine.hip"]
+SOURCES = ["host.hip", "router.hip", "permute.hip", "ffn_gemv.hip", "ffn_mfma.hip", "decode.hip", "combine.hip",
+           "quantize.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",

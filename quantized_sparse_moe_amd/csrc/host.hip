@@ -306,6 +306,21 @@ const char* moe_status_string(moe_status st) {
   return "unknown status";
 }
 
+moe_status moe_quantize_affine(const uint16_t* w_bf16, int64_t rows, int32_t cols, int32_t bits, int32_t group_size,
+                               uint32_t* codes, uint16_t* scales, uint16_t* biases, int32_t* err,
+                               hipStream_t stream) {
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return MOE_ERR_UNSUPPORTED;
+  if (!(group_size == 32 || group_size == 64 || group_size == 128)) return MOE_ERR_UNSUPPORTED;
+  if (cols % group_size != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (w_bf16 == nullptr || codes == nullptr || scales == nullptr || biases == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(biases, 2) ||
+      !aligned(err, 4))
+    return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_quantize_affine(w_bf16, rows, cols, bits, group_size, codes, scales, biases, err, stream));
+}
+
 size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens) {
   if (max_tokens < 0 || check_layer(layer) != MOE_OK) return 0;
   return forward_layout(*layer, max_tokens > 0 ? max_tokens : 1).total;

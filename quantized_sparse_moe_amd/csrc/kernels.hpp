@@ -125,6 +125,10 @@ hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const float* y_slot, const float* w, const float* y_shared, int T, int k, int d,
                           int out_f32, void* out, hipStream_t s);
 
+// Affine quantiser (conversion step before the layer) ------------------------
+hipError_t launch_quantize_affine(const uint16_t* w, int64_t rows, int cols, int bits, int group, uint32_t* codes,
+                                  uint16_t* scales, uint16_t* biases, int32_t* err, hipStream_t s);
+
 // Workspace ------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
 

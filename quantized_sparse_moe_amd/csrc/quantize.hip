@@ -1,0 +1,107 @@
+// Plain min/max affine quantisation of bf16 weights: the conversion step
+// before the layer (model card "mlx-community / DeepSeek-V4-Flash-4bit",
+// section "Conversion": mlx_lm.convert -q --q-bits 4 --q-group-size 64; the
+// "MLX-Serve-mixed-2-3-8bit" card contrasts its calibrated search with plain
+// min/max). Per group of G inputs of a row:
+//   scale = fp16((max - min) / (2^b - 1)), bias = fp16(min),
+//   q = clamp(rint((w - bias) / scale), 0, 2^b - 1)   (q = 0 if scale == 0),
+// every step in fp32 with IEEE rounding (round-to-nearest-even conversions,
+// correctly rounded division, rint ties to even), so the integer codes are
+// reproducible bit for bit. Codes are packed as the layer reads them: one
+// LSB-first bit stream over little-endian uint32 words along the row.
+#include <hip/hip_fp16.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qsmoe {
+
+// One lane per 32-input chunk: its 32 weights (4 x 16-byte loads), the
+// group's min and max over the G / 32 lanes of the group (consecutive lanes,
+// xor shuffles), its 32 codes into BITS whole words. The first lane of a
+// group writes the group's scale and bias.
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void k_quantize_affine(const uint16_t* __restrict__ w, int64_t nchunks,
+                                                         uint32_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                         uint16_t* __restrict__ biases, int32_t* err) {
+  constexpr int LPG = G / 32;  // lanes per group
+  const int64_t chunk = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const bool valid = chunk < nchunks;
+  const int64_t c = valid ? chunk : nchunks - 1;  // the lanes past the end stay in the shuffles
+  const uint4* src = reinterpret_cast<const uint4*>(w + c * 32);
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 u = src[q];
+    const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * q + 2 * i] = bf16_to_f32(p[i] & 0xffffu);
+      v[8 * q + 2 * i + 1] = bf16_to_f32(p[i] >> 16);
+    }
+  }
+  float lo = v[0], hi = v[0];
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    lo = fminf(lo, v[i]);
+    hi = fmaxf(hi, v[i]);
+    finite = finite && isfinite(v[i]);
+  }
+#pragma unroll
+  for (int o = 1; o < LPG; o <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  constexpr float kLevels = static_cast<float>((1 << BITS) - 1);
+  const __half s16 = __float2half_rn((hi - lo) / kLevels);
+  const __half b16 = __float2half_rn(lo);
+  const float s = __half2float(s16), b = __half2float(b16);
+  if (valid && (!finite || !isfinite(s) || !isfinite(b))) set_device_error(err, 8);
+  uint32_t word[BITS];
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) word[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float t = rintf((v[i] - b) / s);
+    const uint32_t q = s == 0.0f ? 0u : static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), kLevels));
+    const int bit = i * BITS, wi = bit >> 5, off = bit & 31;
+    word[wi] |= q << off;
+    if (off + BITS > 32) word[wi + 1] |= q >> (32 - off);
+  }
+  if (!valid) return;
+  uint32_t* dst = codes + c * BITS;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) dst[j] = word[j];
+  if (c % LPG == 0) {
+    scales[c / LPG] = __half_as_ushort(s16);
+    biases[c / LPG] = __half_as_ushort(b16);
+  }
+}
+
+template <int BITS>
+static void launch_quantize_bits(const uint16_t* w, int64_t nchunks, int group, uint32_t* codes, uint16_t* scales,
+                                 uint16_t* biases, int32_t* err, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((nchunks + 255) / 256));
+  if (group == 32)
+    QSMOE_LAUNCH((k_quantize_affine<BITS, 32>), grid, dim3(256), 0, s, w, nchunks, codes, scales, biases, err);
+  else if (group == 64)
+    QSMOE_LAUNCH((k_quantize_affine<BITS, 64>), grid, dim3(256), 0, s, w, nchunks, codes, scales, biases, err);
+  else
+    QSMOE_LAUNCH((k_quantize_affine<BITS, 128>), grid, dim3(256), 0, s, w, nchunks, codes, scales, biases, err);
+}
+
+hipError_t launch_quantize_affine(const uint16_t* w, int64_t rows, int cols, int bits, int group, uint32_t* codes,
+                                  uint16_t* scales, uint16_t* biases, int32_t* err, hipStream_t s) {
+  const int64_t nchunks = rows * (cols / 32);
+  if (nchunks == 0) return hipSuccess;
+  switch (bits) {
+    case 2: launch_quantize_bits<2>(w, nchunks, group, codes, scales, biases, err, s); break;
+    case 3: launch_quantize_bits<3>(w, nchunks, group, codes, scales, biases, err, s); break;
+    case 4: launch_quantize_bits<4>(w, nchunks, group, codes, scales, biases, err, s); break;
+    default: launch_quantize_bits<8>(w, nchunks, group, codes, scales, biases, err, s); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsmoe

@@ -27,4 +27,5 @@ from .gen import (  # noqa: F401
     gen_x,
     gen_token_ids,
     gen_tid2eid,
+    gen_bf16_weights,
 )

@@ -12,6 +12,7 @@ same slice of the fully stacked tensor:
   key (4,)        tid2eid rows, each a uniform random k-subset  [vocab][k]
   key (5, m)      shared expert projection m (0 gate, 1 up, 2 down)
   key (6, e, m)   routed expert e, projection m
+  key (7, i)      bf16 source weights for the quantiser, N(0, 0.02)
 
 Packed codes are drawn directly as uniform uint32 words: for 2/4/8-bit codes,
 for nibble pairs, and for 3-bit streams whose rows are a whole number of words
@@ -175,6 +176,13 @@ def gen_shared(cfg: MoeConfig) -> Optional[ExpertWeights]:
     ew = _alloc_experts(cfg, 1, shared=True)
     _fill_expert(ew, 0, cfg, (5,))
     return ew
+
+
+def gen_bf16_weights(seed: int, i: int, rows: int, cols: int, std: float = 0.02) -> np.ndarray:
+    """Unquantised bf16 weights (uint16 bits) [rows][cols], N(0, std), the
+    quantiser's input (stream key (7, i) under ``seed``)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(entropy=seed, spawn_key=(7, i))))
+    return f32_to_bf16_bits(rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(std))
 
 
 def gen_router(cfg: MoeConfig):

@@ -154,3 +154,17 @@ def test_stage_entry_points_validate():
                               1 << 30, None) == _lib.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_init(None, 0, None) == _lib.MOE_ERR_WORKSPACE
     assert lib.moe_status_string(-3) == b"misaligned pointer"
+
+
+def test_quantize_affine_validates_before_launch():
+    lib = _lib.load()
+    F = 4096  # fake, aligned device addresses: every call below returns before any launch
+    q = lib.moe_quantize_affine
+    assert q(F, 2, 128, 5, 64, F, F, F, None, None) == _lib.MOE_ERR_UNSUPPORTED        # bits
+    assert q(F, 2, 128, 4, 16, F, F, F, None, None) == _lib.MOE_ERR_UNSUPPORTED        # group
+    assert q(F, 2, 96, 4, 64, F, F, F, None, None) == _lib.MOE_ERR_UNSUPPORTED         # cols % group
+    assert q(F, -1, 128, 4, 64, F, F, F, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert q(None, 0, 128, 4, 64, None, None, None, None, None) == _lib.MOE_OK          # nothing to do
+    assert q(None, 2, 128, 4, 64, F, F, F, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert q(F + 2, 2, 128, 4, 64, F, F, F, None, None) == _lib.MOE_ERR_ALIGNMENT
+    assert q(F, 2, 128, 4, 64, F + 4, F, F, None, None) == _lib.MOE_ERR_ALIGNMENT
