@@ -39,7 +39,7 @@ __all__ = [
     "bf16_bits_to_f64", "round_bf16", "e2m1_decode", "e4m3_decode", "e8m0_decode", "unpack_codes",
     "dequant", "sqrtsoftplus", "silu", "router_logits", "route_topk", "route_hash",
     "combine_weights_for_ids", "permute", "swiglu_expert", "forward", "forward_tokens",
-    "pack_codes", "quantize_affine",
+    "pack_codes", "quantize_affine", "mhc_sinkhorn",
 ]
 
 _BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
@@ -425,3 +425,29 @@ def forward_tokens(layer, x_bits, tokens, ids, round_h: bool = True, expert_cach
         y_sh = swiglu_expert(*_expert_mats(layer.shared), x, round_h)
     y = np.einsum("nk,nkd->nd", w, y_slot) + y_sh
     return w, y_slot, y_sh, y
+
+
+# ----------------------------------------------------------------------------
+# mHC mix matrix (an op beside the MoE layer)
+# ----------------------------------------------------------------------------
+
+def mhc_sinkhorn(logits, iters: int = 10, eps: float = 0.0) -> np.ndarray:
+    """Sinkhorn-normalised hyper-connection mix matrices, one n x n per token.
+
+    [CARD4] "Architecture": the residual stream is hc_mult = 4 parallel copies
+    recombined by a doubly-stochastic, Sinkhorn-normalised mix matrix; [PR1192]
+    review notes: the unfused path is a softmax followed by iterations of a
+    sum and a division (~40 launches per call). READINGS (iteration count and
+    epsilon are not on the pages): softmax over each row, then ``iters``
+    rounds of column normalisation followed by row normalisation, each a
+    division by the sums (+ eps); 10 rounds make the pages' ~40 launches
+    (1 + 10 x 2 x (sum + div)).
+    logits: float [..., n, n] -> float64 [..., n, n]
+    """
+    l = np.asarray(logits, dtype=np.float64)
+    m = np.exp(l - l.max(axis=-1, keepdims=True))
+    m = m / m.sum(axis=-1, keepdims=True)
+    for _ in range(iters):
+        m = m / (m.sum(axis=-2, keepdims=True) + eps)
+        m = m / (m.sum(axis=-1, keepdims=True) + eps)
+    return m

@@ -9,6 +9,7 @@ from tests import test_oracle_formats as F
 from tests import test_oracle_layer as L
 from tests import test_oracle_quant as Q
 from tests import test_oracle_router as R
+from tests import test_oracle_sinkhorn as S
 
 
 def _patch(monkeypatch, name, fn):
@@ -73,6 +74,28 @@ def m_quant_truncate(w_bits, bits, group):
     q = np.clip(np.floor((g - bias.astype(np.float32)[..., None]) / scale.astype(np.float32)[..., None]), 0,
                 (1 << bits) - 1).astype(np.int64).reshape(w.shape)
     return om.pack_codes(q, bits), scale, bias
+
+
+def m_sinkhorn_rows_first(logits, iters=10, eps=0.0):
+    """Rows normalised before columns in each round."""
+    l = np.asarray(logits, dtype=np.float64)
+    m = np.exp(l - l.max(axis=-1, keepdims=True))
+    m = m / m.sum(axis=-1, keepdims=True)
+    for _ in range(iters):
+        m = m / (m.sum(axis=-1, keepdims=True) + eps)
+        m = m / (m.sum(axis=-2, keepdims=True) + eps)
+    return m
+
+
+def m_sinkhorn_no_max_shift(logits, iters=10, eps=0.0):
+    l = np.asarray(logits, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        m = np.exp(l)
+        m = m / m.sum(axis=-1, keepdims=True)
+        for _ in range(iters):
+            m = m / (m.sum(axis=-2, keepdims=True) + eps)
+            m = m / (m.sum(axis=-1, keepdims=True) + eps)
+    return m
 
 
 def m_e8m0_off_by_one(b):
@@ -165,6 +188,8 @@ MUTATIONS = [
     ("route_hash", m_hash_sorted_ids, [R.check_hash_route_lookup]),
     ("quantize_affine", m_quant_levels_pow2, [Q.check_grid_roundtrip, Q.check_quant_bounds]),
     ("quantize_affine", m_quant_truncate, [Q.check_quant_bounds]),
+    ("mhc_sinkhorn", m_sinkhorn_rows_first, [S.check_sinkhorn_properties]),
+    ("mhc_sinkhorn", m_sinkhorn_no_max_shift, [S.check_sinkhorn_properties]),
 ]
 
 
