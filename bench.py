@@ -39,7 +39,8 @@ def parse():
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=16)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8", "stack43", "quantize"])
+                   choices=["decode", "tiny", "hash", "prefill", "mixed", "mxfp8", "stack43", "quantize",
+                            "sinkhorn"])
     p.add_argument("--copies", type=int, default=0, help="device copies of the layer to rotate over (0: auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the CPU oracle sample")
@@ -251,6 +252,86 @@ def main_quantize(args):
     print(json.dumps(rec), flush=True)
 
 
+def main_sinkhorn(args):
+    """mHC mix matrices of a 4096-token batch (4 x 4 per token, 10 rounds): the
+    fused kernel, one launch per step; the unfused torch loop (a softmax and
+    four launches per round) is timed beside it for context."""
+    import numpy as np
+    import torch
+    import quantized_sparse_moe_amd as qm
+
+    qm.load()
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, n, iters = 4096, 4, 10
+    rng = np.random.default_rng(31)
+    l = torch.from_numpy(rng.standard_normal((T, n, n)).astype(np.float32)).to(dev)
+    out = torch.empty_like(l)
+    K, W = args.steps, args.warmup
+
+    def timed(fn):
+        """K calls captured once as a HIP graph, replayed between events (host
+        launch overhead outside the timed region, as for the layer)."""
+        for _ in range(W):
+            fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(graph, stream=st):
+                for _ in range(K):
+                    fn()
+        torch.cuda.current_stream().wait_stream(st)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
+    def unfused():
+        m = torch.softmax(l, dim=-1)
+        for _ in range(iters):
+            m = m / m.sum(dim=-2, keepdim=True)
+            m = m / m.sum(dim=-1, keepdim=True)
+        return m
+
+    ms = timed(lambda: qm.mhc_sinkhorn(l, iters, 0.0, out=out))
+    ms_unfused = timed(unfused)
+    nbytes = T * n * n * 4 * 2
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": "mHC Sinkhorn mix matrices/s (op beside the MoE layer)", "value": T / (ms * 1e-3),
+        "unit": "matrices/s", "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"sinkhorn: {T} tokens x {n}x{n} fp32 logits N(0,1), {iters} rounds, eps 0",
+                   "timing": "hipgraph, one launch per step", "unfused_torch_ms": ms_unfused,
+                   "speedup_vs_unfused": ms_unfused / ms},
+        "roofline": {"bound": "hbm", "kernel": "k_mhc_sinkhorn", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(args.workload, "k_mhc_sinkhorn"),
+                     "algorithmic_bytes_per_launch": nbytes, "avg_launch_us": ms * 1e3,
+                     "note": "0.5 MB per launch: bound by launch and memory latency, not HBM bandwidth"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        ln = l.cpu().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 2.0:
+            oracle.mhc_sinkhorn(ln, iters)
+            reps += 1
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": reps * T / el, "unit": "matrices/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} oracle calls on the {T}-token batch ({el:.1f} s)",
+                               "host_cpus": len(os.sched_getaffinity(0))}
+    print(json.dumps(rec), flush=True)
+
+
 def main_stack(args):
     """One decode token through the 43 MoE layers of the model (each layer with
     its own experts, formats and expert count, and its own seeded activations:
@@ -409,6 +490,9 @@ def main():
         return
     if args.workload == "quantize":
         main_quantize(args)
+        return
+    if args.workload == "sinkhorn":
+        main_sinkhorn(args)
         return
 
     import quantized_sparse_moe_amd as qm

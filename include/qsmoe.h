@@ -262,6 +262,26 @@ moe_status moe_quantize_affine(const uint16_t* w_bf16, int64_t rows, int32_t col
                                uint32_t* codes, uint16_t* scales, uint16_t* biases, int32_t* err,
                                hipStream_t stream);
 
+/*
+ * mHC mix matrices (an op beside the MoE layer): [CARD4] "Architecture": the
+ * residual stream is hc_mult = 4 parallel copies recombined by a
+ * doubly-stochastic, Sinkhorn-normalised mix matrix; [PR1192] review notes:
+ * unfused, a softmax followed by iterations of a sum and a division (~40
+ * launches per call). For each of T tokens: m = softmax over each row of the
+ * n x n logits, then `iters` rounds of dividing each column by its sum + eps
+ * and then each row by its sum + eps (the pages give neither the round count
+ * nor eps; 10 rounds and eps = 0 make the pages' ~40 unfused launches). fp32,
+ * one launch, allocates nothing.
+ *   logits : device fp32 [T][n][n]
+ *   out    : device fp32 [T][n][n] (may be logits itself)
+ * n in {2, 4, 8}; T >= 0; iters >= 0; eps >= 0 and finite. Rows whose
+ * softmax leaves a column all zero (logit spreads beyond ~80 in fp32) give
+ * NaN when eps = 0. Errors: INVALID_ARG, UNSUPPORTED (n), ALIGNMENT (4-byte),
+ * HIP.
+ */
+moe_status moe_mhc_sinkhorn(const float* logits, int64_t T, int32_t n, int32_t iters, float eps, float* out,
+                            hipStream_t stream);
+
 const char* moe_status_string(moe_status status);
 
 /* Library version string. */

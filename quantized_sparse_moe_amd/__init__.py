@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     forward,
     forward_probed,
     forward_staged,
+    mhc_sinkhorn,
     permute,
     quantize_affine,
     route,

@@ -184,6 +184,20 @@ def quantize_affine(w: torch.Tensor, bits: int, group: int, err: Optional[torch.
     return codes, scales, biases
 
 
+def mhc_sinkhorn(logits: torch.Tensor, iters: int = 10, eps: float = 0.0, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """mHC mix matrices (moe_mhc_sinkhorn): logits fp32 [T][n][n] -> fp32 [T][n][n]."""
+    if logits.dtype != torch.float32 or not logits.is_cuda or not logits.is_contiguous() or logits.dim() != 3:
+        raise ValueError("logits must be a contiguous fp32 device tensor [T][n][n]")
+    T, n, n2 = logits.shape
+    if n != n2:
+        raise ValueError("mix matrices must be square")
+    out = torch.empty_like(logits) if out is None else out
+    check(_lib.load().moe_mhc_sinkhorn(_ptr(logits), T, n, iters, eps, _ptr(out), _stream(stream)),
+          "moe_mhc_sinkhorn")
+    return out
+
+
 def permute(ids: torch.Tensor, num_experts: int, ws: torch.Tensor, stream=None):
     T, k = ids.shape
     offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=ids.device)

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libqsmoe.so")
 ARCH = "gfx950"
 
 SOURCES = ["host.hip", "router.hip", "permute.hip", "ffn_gemv.hip", "ffn_mfma.hip", "decode.hip", "combine.hip",
-           "quantize.hip"]
+           "quantize.hip", "sinkhorn.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -321,6 +321,16 @@ moe_status moe_quantize_affine(const uint16_t* w_bf16, int64_t rows, int32_t col
   return hip_status(launch_quantize_affine(w_bf16, rows, cols, bits, group_size, codes, scales, biases, err, stream));
 }
 
+moe_status moe_mhc_sinkhorn(const float* logits, int64_t T, int32_t n, int32_t iters, float eps, float* out,
+                            hipStream_t stream) {
+  if (T < 0 || iters < 0 || !(eps >= 0.0f) || eps == INFINITY) return MOE_ERR_INVALID_ARG;
+  if (!(n == 2 || n == 4 || n == 8)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (logits == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(out, 4)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_mhc_sinkhorn(logits, T, n, iters, eps, out, stream));
+}
+
 size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens) {
   if (max_tokens < 0 || check_layer(layer) != MOE_OK) return 0;
   return forward_layout(*layer, max_tokens > 0 ? max_tokens : 1).total;

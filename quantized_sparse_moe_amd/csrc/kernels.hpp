@@ -129,6 +129,10 @@ hipError_t launch_combine(const float* y_slot, const float* w, const float* y_sh
 hipError_t launch_quantize_affine(const uint16_t* w, int64_t rows, int cols, int bits, int group, uint32_t* codes,
                                   uint16_t* scales, uint16_t* biases, int32_t* err, hipStream_t s);
 
+// mHC Sinkhorn mix matrices -------------------------------------------------
+hipError_t launch_mhc_sinkhorn(const float* logits, int64_t T, int n, int iters, float eps, float* out,
+                               hipStream_t s);
+
 // Workspace ------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
 

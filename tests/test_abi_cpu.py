@@ -168,3 +168,17 @@ def test_quantize_affine_validates_before_launch():
     assert q(None, 2, 128, 4, 64, F, F, F, None, None) == _lib.MOE_ERR_INVALID_ARG
     assert q(F + 2, 2, 128, 4, 64, F, F, F, None, None) == _lib.MOE_ERR_ALIGNMENT
     assert q(F, 2, 128, 4, 64, F + 4, F, F, None, None) == _lib.MOE_ERR_ALIGNMENT
+
+
+def test_mhc_sinkhorn_validates_before_launch():
+    lib = _lib.load()
+    F = 4096
+    s = lib.moe_mhc_sinkhorn
+    assert s(F, 8, 3, 10, 0.0, F, None) == _lib.MOE_ERR_UNSUPPORTED          # n
+    assert s(F, -1, 4, 10, 0.0, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert s(F, 8, 4, -1, 0.0, F, None) == _lib.MOE_ERR_INVALID_ARG          # iters
+    assert s(F, 8, 4, 10, -1.0, F, None) == _lib.MOE_ERR_INVALID_ARG         # eps
+    assert s(F, 8, 4, 10, float("nan"), F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert s(None, 0, 4, 10, 0.0, None, None) == _lib.MOE_OK                 # nothing to do
+    assert s(None, 8, 4, 10, 0.0, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert s(F + 2, 8, 4, 10, 0.0, F, None) == _lib.MOE_ERR_ALIGNMENT
