@@ -41,12 +41,10 @@ __global__ __launch_bounds__(256) void k_quantize_affine(const uint16_t* __restr
     }
   }
   float lo = v[0], hi = v[0];
-  bool finite = true;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     lo = fminf(lo, v[i]);
     hi = fmaxf(hi, v[i]);
-    finite = finite && isfinite(v[i]);
   }
 #pragma unroll
   for (int o = 1; o < LPG; o <<= 1) {
@@ -57,18 +55,37 @@ __global__ __launch_bounds__(256) void k_quantize_affine(const uint16_t* __restr
   const __half s16 = __float2half_rn((hi - lo) / kLevels);
   const __half b16 = __float2half_rn(lo);
   const float s = __half2float(s16), b = __half2float(b16);
-  if (valid && (!finite || !isfinite(s) || !isfinite(b))) set_device_error(err, 8);
   uint32_t word[BITS];
 #pragma unroll
   for (int j = 0; j < BITS; ++j) word[j] = 0;
+  // rint of the correctly rounded quotient without a division per weight:
+  // with r the correctly rounded 1 / s, d * r lies within 1.5 * 2^-23 * |d / s|
+  // of the rounded quotient, so both round to the same integer unless d * r is
+  // that close to a half-integer. |d * r| is at most tmax (the rounding steps
+  // are monotonic and every finite weight lies in [lo, hi]), which gives one
+  // distance for the lane, with margin. Only weights closer than that to a
+  // half-integer, and all of a group with scale 0, a non-finite scale or
+  // NaN weights (whose test fails), take the division.
+  const float r = 1.0f / s;
+  const float tmax = fmaxf(fabsf(lo - b), fabsf(hi - b)) * r;
+  const float lim = (s > 0.0f && tmax < 0x1p18f) ? 0.5f - fmaxf(tmax, 1.0f) * 0x1p-21f : -1.0f;
+  bool finite = true;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float t = rintf((v[i] - b) / s);
-    const uint32_t q = s == 0.0f ? 0u : static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), kLevels));
+    const float d = v[i] - b;
+    const float tr = d * r;
+    float t = rintf(tr);
+    if (!(fabsf(tr - t) < lim)) {
+      t = s == 0.0f ? 0.0f : rintf(d / s);
+      finite = finite && isfinite(v[i]);
+    }
+    const uint32_t q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), kLevels));
     const int bit = i * BITS, wi = bit >> 5, off = bit & 31;
     word[wi] |= q << off;
     if (off + BITS > 32) word[wi + 1] |= q >> (32 - off);
   }
+  // infinities show in the scale or the bias; NaN weights only here
+  if (valid && (!finite || !isfinite(s) || !isfinite(b))) set_device_error(err, 8);
   if (!valid) return;
   uint32_t* dst = codes + c * BITS;
 #pragma unroll

@@ -52,6 +52,37 @@ def test_quantize_matches_oracle(bits, group):
     assert np.array_equal(biases.view(np.uint16), rb.view(np.uint16))
 
 
+def _tie_rows(bits, group, cols):
+    """Groups whose quotients (w - bias) / scale land exactly on half-integers,
+    and one bf16 step either side of them: min 0 and max (2^b - 1) / 16 make
+    the scale exactly 1/16, so w = (2k + 1) / 32 gives the quotient k + 1/2."""
+    levels = (1 << bits) - 1
+    ks = np.arange(min(levels, 128))
+    ties = (2 * ks + 1) / 32.0
+    rows = []
+    for nudge in (0, 1, -1):
+        g = np.resize(ties, group).astype(np.float32)
+        g[0], g[1] = 0.0, levels / 16.0
+        b = f32_to_bf16_bits(g).astype(np.int32)
+        b[2:] += nudge          # one bf16 step up or down (all values positive)
+        rows.append(np.tile(b.astype(np.uint16), cols // group))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (3, 64), (4, 64), (8, 128)])
+def test_quantize_exact_and_near_ties(bits, group):
+    """Exact ties round to even, neighbours one step away to their side: the
+    same integers as the oracle's correctly rounded division."""
+    w = _tie_rows(bits, group, 2 * group)
+    codes, scales, biases, err = _gpu_quant(w, bits, group)
+    rc, rs, rb = oracle.quantize_affine(w, bits, group)
+    assert err == 0
+    assert np.all(rs.astype(np.float32)[:1] == 1.0 / 16)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(scales.view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(biases.view(np.uint16), rb.view(np.uint16))
+
+
 def test_quantize_ragged_tail_and_one_row():
     """Chunk counts that leave the last workgroup partly empty, and a single row."""
     for rows, cols, bits, group in [(3, 4096 + 64, 4, 64), (1, 64, 2, 64), (257, 96, 3, 32)]:
