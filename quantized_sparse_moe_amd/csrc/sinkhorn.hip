@@ -7,16 +7,55 @@
 // call). Per token: softmax over each row of the n x n logits, then `iters`
 // rounds of dividing every column by its sum (+ eps) and then every row by
 // its sum (+ eps). One lane per matrix element: a token's n x n lanes are
-// consecutive within a wave (n * n divides 64), so a row sum is an xor
-// shuffle over the n lanes of the row and a column sum one over the lanes n
-// apart; the logits are read once (coalesced) and the result written once,
-// in one launch. (One thread per token, its matrix in registers, ran each
+// consecutive within a wave (n * n divides 64), so a row sum pairs the n
+// lanes of the row and a column sum the lanes n apart, by DPP lane moves
+// within 16 lanes (only n = 8's column steps across 16 and 32 lanes go
+// through LDS shuffles); the logits are read once (coalesced) and the result
+// written once, in one launch. (With every step an LDS shuffle, a chain of
+// 40 round trips over 10 rounds, 4096 tokens at n = 4 took 3.9-4.5 us.) (One thread per token, its matrix in registers, ran each
 // token's ~300 divisions in one dependent chain on 1/16 of the lanes: 10.4 us
 // per 4096 tokens.)
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qsmoe {
+
+// A lane's value moved by a DPP lane pattern (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4e;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within 8
+constexpr int kDppRor4 = 0x124;       // rotate by 4 within 16
+constexpr int kDppRor8 = 0x128;       // rotate by 8 within 16
+
+// Sum over the N consecutive lanes of a matrix row: every lane of the row
+// gets the same bits (each step adds a lane's value and its partner's).
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_mov<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp_mov<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp_mov<kDppHalfMirror>(x);
+  return x;
+}
+
+// Sum over the N lanes of a matrix column (stride N, NN lanes per matrix).
+template <int N>
+__device__ __forceinline__ float col_sum(float x) {
+  if constexpr (N == 2) {
+    x += dpp_mov<kDppXor2>(x);
+  } else if constexpr (N == 4) {
+    x += dpp_mov<kDppRor8>(x);  // lanes i, i + 8 of the 16
+    x += dpp_mov<kDppRor4>(x);  // ... and i + 4, i + 12
+  } else {
+    x += dpp_mov<kDppRor8>(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+  }
+  return x;
+}
 
 template <int N>
 __global__ __launch_bounds__(256) void k_mhc_sinkhorn(const float* logits, int64_t T, int iters, float eps,
@@ -27,22 +66,14 @@ __global__ __launch_bounds__(256) void k_mhc_sinkhorn(const float* logits, int64
   const bool valid = e < T * NN;  // whole matrices are valid or not: 256 % NN == 0
   float v = valid ? logits[e] : 0.0f;
   float mx = v;
-#pragma unroll
-  for (int o = 1; o < N; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  mx = fmaxf(mx, dpp_mov<kDppXor1>(mx));
+  if constexpr (N >= 4) mx = fmaxf(mx, dpp_mov<kDppXor2>(mx));
+  if constexpr (N >= 8) mx = fmaxf(mx, dpp_mov<kDppHalfMirror>(mx));
   v = expf(v - mx);
-  float s = v;
-#pragma unroll
-  for (int o = 1; o < N; o <<= 1) s += __shfl_xor(s, o);
-  v = v / s;
+  v = v / row_sum<N>(v);
   for (int it = 0; it < iters; ++it) {
-    float c = v;
-#pragma unroll
-    for (int o = N; o < NN; o <<= 1) c += __shfl_xor(c, o);
-    v = v / (c + eps);
-    float r = v;
-#pragma unroll
-    for (int o = 1; o < N; o <<= 1) r += __shfl_xor(r, o);
-    v = v / (r + eps);
+    v = v / (col_sum<N>(v) + eps);
+    v = v / (row_sum<N>(v) + eps);
   }
   if (valid) out[e] = v;
 }

@@ -1,7 +1,8 @@
 """HIP-graph capture of whole steps (the way bench.py times them): a graph of
 several steps, replayed several times with the program's own eager work and
 synchronisations in between, gives on every replay exactly the eager outputs.
-Covers the fused decode path, the GEMV path and both matrix-core paths."""
+Covers the fused decode path (top-k and hash routed), the GEMV path and the
+matrix-core paths (MXFP4, affine, MXFP8)."""
 import numpy as np
 import pytest
 import torch
@@ -18,6 +19,8 @@ CASES = [
     variant("mixed", "graph_gemv", 302, T=16, d=512, I=256, E=32, I_shared=256, steps=3),
     variant("prefill", "graph_mx", 303, T=128, d=512, I=256, E=8, top_k=2, bias_kind="normal", steps=3),
     variant("hash", "graph_aff", 304, T=48, d=512, I=256, E=16, vocab=1000, steps=3),
+    variant("hash", "graph_hash_dec", 305, T=1, d=512, I=256, E=16, vocab=1000, steps=3),
+    variant("mxfp8", "graph_mxfp8", 306, T=64, d=512, I=256, E=16, steps=3),
 ]
 
 

@@ -44,3 +44,35 @@ def test_sinkhorn_large_logits_and_empty():
     ref = oracle.mhc_sinkhorn(l, 10)
     assert np.all(np.isfinite(got)) and np.all(np.abs(got - ref) <= 1e-5 * ref + 1e-7)
     assert qm.mhc_sinkhorn(torch.empty((0, 4, 4), device="cuda")).shape == (0, 4, 4)
+
+
+def test_sinkhorn_graph_replays_equal_eager():
+    """Several calls captured as one HIP graph (the way the op is timed),
+    replayed three times with eager work in between: every replay gives the
+    eager results bit for bit."""
+    rng = np.random.default_rng(93)
+    ls = [torch.from_numpy(rng.standard_normal((300, 4, 4)).astype(np.float32)).cuda() for _ in range(3)]
+    eager = [qm.mhc_sinkhorn(l, 10, 0.0).clone() for l in ls]
+    outs = [torch.empty_like(l) for l in ls]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for l, o in zip(ls, outs):
+                qm.mhc_sinkhorn(l, 10, 0.0, out=o)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    scratch = torch.empty(1 << 20, device="cuda")
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(len(ls)):
+            assert torch.equal(outs[i], eager[i]), (rep, i)
+        scratch.normal_()
+        again = qm.mhc_sinkhorn(ls[rep], 10, 0.0)
+        torch.cuda.synchronize()
+        assert torch.equal(again, eager[rep])
