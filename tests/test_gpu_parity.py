@@ -132,6 +132,30 @@ def test_small_layer_parity(cfg):
     print(f"{cfg.name}: max rel err {worst:.2e}")
 
 
+# The documented maxima: hidden (gate/up input width) 8192 on every path (the
+# fused decode path at four 32-input chunks per lane, the streaming GEMV, the
+# matrix-core GEMM), 1024 experts with top-8 (above the fused path's 256, so
+# the general path at one token too), intermediate (down input width) 8192.
+LIMITS = [
+    variant("decode", "lim_d8192_fused_t1", 140, T=1, d=8192, I=128, E=16, top_k=4, I_shared=128),
+    variant("decode", "lim_d8192_fused_t3", 141, T=3, d=8192, I=128, E=16, top_k=4, I_shared=128),
+    variant("mixed", "lim_d8192_gemv", 142, T=6, d=8192, I=128, E=64, top_k=4, I_shared=128),
+    variant("hash", "lim_d8192_mfma", 143, T=160, d=8192, I=128, E=8, vocab=1000),
+    variant("tiny", "lim_E1024_t1", 144, T=1, d=256, I=128, E=1024, top_k=8),
+    variant("tiny", "lim_E1024_t40", 145, T=40, d=256, I=128, E=1024, top_k=8),
+    variant("decode", "lim_I8192_t2", 146, T=2, d=256, I=8192, E=4, top_k=2, I_shared=8192),
+    variant("decode", "lim_I8192_t40", 147, T=40, d=256, I=8192, E=4, top_k=2, I_shared=8192),
+]
+
+
+@pytest.mark.parametrize("cfg", LIMITS, ids=[c.name for c in LIMITS])
+def test_maximum_size_parity(cfg):
+    layer = synth.gen_layer(cfg)
+    dl = qm.DeviceLayer.from_host(layer)
+    worst = check_layer(cfg, layer, dl, 0)
+    print(f"{cfg.name}: max rel err {worst:.2e}")
+
+
 @pytest.mark.parametrize("T,d,E", [(600, 1024, 64), (300, 1024, 64), (100, 1056, 40), (17, 4096, 256)])
 def test_router_logits_and_topk_on_gpu_keys(T, d, E):
     """Logits within fp32 accumulation error of float64; the GPU top-k equals
