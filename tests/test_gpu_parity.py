@@ -156,6 +156,31 @@ def test_maximum_size_parity(cfg):
     print(f"{cfg.name}: max rel err {worst:.2e}")
 
 
+# Every token routed to the same k experts (k buckets full, the rest empty):
+# a bias far above the scores on experts 0..k-1 (the bias only ranks, so the
+# weights are still the scores'), or a hash table whose rows all name them.
+ONE_BUCKET = [
+    variant("prefill", "same_mxfp4_mfma", 150, T=300, d=256, I=128, E=8, top_k=2, bias_kind="normal"),
+    variant("hash", "same_hash_aff4_mfma", 151, T=96, d=512, I=256, E=16, vocab=500),
+    variant("mixed", "same_gemv", 152, T=6, d=512, I=256, E=64, top_k=4, I_shared=128),
+    variant("decode", "same_fused_t4", 153, T=4, d=512, I=256, E=32, I_shared=128),
+]
+
+
+@pytest.mark.parametrize("cfg", ONE_BUCKET, ids=[c.name for c in ONE_BUCKET])
+def test_all_tokens_in_the_same_buckets(cfg):
+    layer = synth.gen_layer(cfg)
+    k = cfg.top_k
+    if cfg.route == "hash":
+        layer.tid2eid[:] = np.arange(k, dtype=layer.tid2eid.dtype)
+    else:
+        layer.bias[:k] += 10.0
+    dl = qm.DeviceLayer.from_host(layer)
+    check_layer(cfg, layer, dl, 0)
+    ids = oracle.forward(layer, synth.gen_x(cfg, 0), token_ids=synth.gen_token_ids(cfg, 0)).ids
+    assert np.array_equal(np.sort(ids, axis=1), np.tile(np.arange(k), (cfg.T, 1)))
+
+
 @pytest.mark.parametrize("T,d,E", [(600, 1024, 64), (300, 1024, 64), (100, 1056, 40), (17, 4096, 256)])
 def test_router_logits_and_topk_on_gpu_keys(T, d, E):
     """Logits within fp32 accumulation error of float64; the GPU top-k equals
