@@ -181,6 +181,31 @@ def test_all_tokens_in_the_same_buckets(cfg):
     assert np.array_equal(np.sort(ids, axis=1), np.tile(np.arange(k), (cfg.T, 1)))
 
 
+# All router weights zero and no bias: every logit is exactly 0, every key
+# ties, so each token takes experts 0..k-1 in that order with weights 1/k (the
+# ties-to-the-lower-index rule, in closed form) on every router path: the
+# fused decode path (its output checked against the staged entry points),
+# the K-split and the 64 x 64 logits kernels.
+ALL_TIED = [
+    variant("decode", "tied_fused_t1", 160, T=1, d=512, I=256, E=32, I_shared=128, bias_kind="none"),
+    variant("decode", "tied_fused_t3", 161, T=3, d=512, I=256, E=32, I_shared=128, bias_kind="none"),
+    variant("tiny", "tied_ksplit_t40", 162, T=40, d=256, I=128, E=64, top_k=6, bias_kind="none"),
+    variant("prefill", "tied_mfma_t600", 163, T=600, d=256, I=128, E=8, top_k=2, bias_kind="none"),
+]
+
+
+@pytest.mark.parametrize("cfg", ALL_TIED, ids=[c.name for c in ALL_TIED])
+def test_all_keys_tied_pick_the_lowest_experts(cfg):
+    layer = synth.gen_layer(cfg)
+    layer.wr[:] = 0.0
+    dl = qm.DeviceLayer.from_host(layer)
+    check_layer(cfg, layer, dl, 0)
+    st, _, _, _ = run_staged(dl, synth.gen_x(cfg, 0))
+    k = cfg.top_k
+    assert np.array_equal(st.ids.cpu().numpy(), np.tile(np.arange(k, dtype=np.int32), (cfg.T, 1)))
+    assert np.allclose(st.w.cpu().numpy(), 1.0 / k, rtol=1e-6, atol=0)
+
+
 @pytest.mark.parametrize("T,d,E", [(600, 1024, 64), (300, 1024, 64), (100, 1056, 40), (17, 4096, 256)])
 def test_router_logits_and_topk_on_gpu_keys(T, d, E):
     """Logits within fp32 accumulation error of float64; the GPU top-k equals
