@@ -58,25 +58,28 @@ __global__ __launch_bounds__(256) void k_quantize_affine(const uint16_t* __restr
   uint32_t word[BITS];
 #pragma unroll
   for (int j = 0; j < BITS; ++j) word[j] = 0;
-  // rint of the correctly rounded quotient without a division per weight:
-  // with r the correctly rounded 1 / s, d * r lies within 1.5 * 2^-23 * |d / s|
-  // of the rounded quotient, so both round to the same integer unless d * r is
-  // that close to a half-integer. |d * r| is at most tmax (the rounding steps
-  // are monotonic and every finite weight lies in [lo, hi]), which gives one
-  // distance for the lane, with margin. Only weights closer than that to a
-  // half-integer, and all of a group with scale 0, a non-finite scale or
-  // NaN weights (whose test fails), take the division.
+  // rint of the correctly rounded quotient fl(fl(w - b) / s) without a
+  // subtraction and a division per weight: with r the correctly rounded 1 / s,
+  // tr = fma(w, r, -fl(b r)) lies within 2^-22 |(w - b) / s| + 2^-24 |b r| of
+  // that quotient, so both round to the same integer unless tr is that close
+  // to a half-integer. |(w - b) / s| is at most tmax (the rounding steps are
+  // monotonic and every finite weight lies in [lo, hi]), which gives one
+  // distance for the lane, with a 4x margin. Only weights closer than that to
+  // a half-integer, and all of a group with scale 0, a non-finite scale, an
+  // offset so large that the distance reaches 1/4, or NaN weights (whose test
+  // fails), take the subtraction and the division.
   const float r = 1.0f / s;
+  const float br = b * r;
   const float tmax = fmaxf(fabsf(lo - b), fabsf(hi - b)) * r;
-  const float lim = (s > 0.0f && tmax < 0x1p18f) ? 0.5f - fmaxf(tmax, 1.0f) * 0x1p-21f : -1.0f;
+  const float tol = (fmaxf(tmax, 1.0f) + fabsf(br)) * 0x1p-20f;
+  const float lim = (s > 0.0f && tol < 0.25f) ? 0.5f - tol : -1.0f;
   bool finite = true;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const float d = v[i] - b;
-    const float tr = d * r;
+    const float tr = fmaf(v[i], r, -br);
     float t = rintf(tr);
     if (!(fabsf(tr - t) < lim)) {
-      t = s == 0.0f ? 0.0f : rintf(d / s);
+      t = s == 0.0f ? 0.0f : rintf((v[i] - b) / s);
       finite = finite && isfinite(v[i]);
     }
     const uint32_t q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), kLevels));
