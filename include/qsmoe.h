@@ -171,25 +171,67 @@ typedef struct {
   const moe_experts* shared;
 } moe_layer;
 
-/* Bytes of workspace moe_forward needs for up to max_tokens tokens (0 on an
- * invalid layer). The same size serves every other entry point. */
+/* Bytes of workspace moe_forward needs for every token count up to
+ * max_tokens (0 on an invalid layer): never smaller for a larger max_tokens,
+ * so a buffer sized once (e.g. before graph capture) serves every T <=
+ * max_tokens. The same size serves every other entry point. */
 size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens);
+
+/*
+ * Where moe_forward keeps its intermediates in the workspace, for inspection
+ * after the call (tests, routing statistics). Byte offsets from the start of
+ * `ws`; 0 marks a region the call does not write for this layer and T.
+ *   ids      int32 [T][k]   routed expert ids, slot order (key descending)
+ *   weights  fp32  [T][k]   combine weights
+ *   logits   fp32  [T][E]   router logits (top-k routing; hash routing on the
+ *                           fused path only)
+ *   keys     uint64 [T][E]  ranking key of every expert: bits 63..32 are the
+ *                           fp32 key s + bias mapped so that unsigned order is
+ *                           numeric order (key >= 0: bits | 0x80000000; key < 0:
+ *                           ~bits), bits 31..0 are 0xFFFFFFFF - e; the top-k
+ *                           takes the k largest values (ties: lower index)
+ *   scores   fp32  [T][E]   sqrtsoftplus scores s of every expert
+ *   offsets  int32 [E+1], perm int32 [T*k]   buckets (general path only)
+ *   h        bf16  [T*k][I]  silu(gate) * up rounded to bf16: bucket order
+ *                           (row p belongs to assignment perm[p]) on the
+ *                           general path, slot order t*k + j on the fused path
+ *   h_shared bf16  [T][I_shared] (shared expert)
+ *   y_slot   fp32  [T*k][d], y_shared fp32 [T][d]  (general path only)
+ * fused = 1 when moe_forward takes the three-launch small-batch path. total =
+ * the bytes moe_forward needs for exactly T tokens. Errors: INVALID_ARG (T <
+ * 1, null out, invalid layer), UNSUPPORTED.
+ */
+typedef struct {
+  size_t total;
+  size_t ids, weights, logits, keys, scores, offsets, perm, h, h_shared, y_slot, y_shared;
+  int32_t fused;
+} moe_ws_layout;
+
+moe_status moe_workspace_layout(const moe_layer* layer, int32_t T, moe_ws_layout* out);
 
 /* Zero the workspace header, which holds the device error word (a small
  * kernel; capturable). */
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Step 1. x_bf16 [T][hidden]; token_ids int32 [T] (hash mode, else may be
- * NULL); outputs topk_ids int32 [T][top_k], topk_w fp32 [T][top_k]. ws needs
- * 256 + 4*T*E bytes (top-k mode logits). */
+/* Step 1 (the router as moe_router defines it). x_bf16 [T][hidden];
+ * token_ids int32 [T] (hash mode, else may be NULL); outputs topk_ids int32
+ * [T][top_k], topk_w fp32 [T][top_k]. In top-k mode ws needs 256 + A(4*T*E)
+ * + A(8*T*E) + A(4*T*E) bytes, A() rounding up to a multiple of 256, and
+ * holds after the call: logits fp32 [T][E] at byte 256, then the packed
+ * ranking keys uint64 [T][E] and the scores fp32 [T][E] (formats as in
+ * moe_ws_layout). Hash mode needs 256 bytes. */
 moe_status moe_route(const moe_router* router, const uint16_t* x_bf16, const int32_t* token_ids,
                      int32_t T, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
 /* Step 2. A stable counting sort of the T*k assignments a = t*k + j by
- * expert topk_ids[a]: expert_offsets int32 [E+1] (exclusive prefix sum of the
+ * expert topk_ids[a], so that each of the stacked experts ([PR1192]: experts
+ * pre-stacked as switch_mlp.{gate,up,down}_proj, one weight tensor per
+ * projection over all experts) runs once over one contiguous bucket of its
+ * assignments: expert_offsets int32 [E+1] (exclusive prefix sum of the
  * per-expert counts; offsets[E] = T*k), perm int32 [T*k] (assignment indices
- * bucketed by expert, ascending within a bucket). ws needs 256 bytes. */
+ * bucketed by expert, ascending within a bucket). Ids outside [0, E) set
+ * MOE_DEVERR_EXPERT_ID and count as expert 0. ws needs 256 bytes. */
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E,
                        int32_t* expert_offsets, int32_t* perm, void* ws, size_t ws_bytes,
                        hipStream_t stream);
@@ -205,9 +247,17 @@ moe_status moe_expert_ffn(const moe_experts* routed, const moe_experts* shared,
                           const int32_t* expert_offsets, const int32_t* perm, float* y_slot,
                           float* y_shared, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Step 4. out[t] = sum_{j=0..k-1} topk_w[t][j] * y_slot[t*k + j] (j in
- * order) + y_shared[t] (if non-NULL), accumulated in fp32; stored as bf16
- * (round to nearest even) or fp32 per out_dtype. d % 4 == 0. */
+/* Step 4. The weighted combine: each token's output is its selected
+ * experts' outputs times their router weights ([ALPHA] "REAP-pruned builds":
+ * router weight x expert output, renormalised over the kept experts), plus
+ * the shared expert's output ([ALPHA] "Why mixed-4_8bit"):
+ * out[t] = sum_{j=0..k-1} topk_w[t][j] * y_slot[t*k + j] (j in order) +
+ * y_shared[t] (if non-NULL), accumulated in fp32 with one writer per output
+ * element (no atomics); stored as bf16 (round to nearest even) or fp32 per
+ * out_dtype. y_slot fp32 [T*k][d], topk_w fp32 [T][k], y_shared fp32 [T][d]
+ * or NULL, out [T][d]. d % 4 == 0; y_slot, y_shared 16-byte aligned, out
+ * 8-byte (bf16) or 16-byte (fp32) aligned. Errors: INVALID_ARG, UNSUPPORTED
+ * (d), ALIGNMENT, HIP. */
 moe_status moe_combine(const float* y_slot, const float* topk_w, const float* y_shared, int32_t T,
                        int32_t k, int32_t d, int32_t out_dtype, void* out, hipStream_t stream);
 

@@ -38,7 +38,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "round_bf16", "e2m1_decode", "e4m3_decode", "e8m0_decode", "unpack_codes",
     "dequant", "sqrtsoftplus", "silu", "router_logits", "route_topk", "route_hash",
-    "combine_weights_for_ids", "permute", "swiglu_expert", "forward", "forward_tokens",
+    "combine_weights_for_ids", "permute", "swiglu_h", "expert_mats", "swiglu_expert", "forward", "forward_tokens",
     "pack_codes", "quantize_affine", "mhc_sinkhorn",
 ]
 
@@ -322,23 +322,33 @@ def permute(ids: np.ndarray, E: int):
 # Experts and combine
 # ----------------------------------------------------------------------------
 
+def swiglu_h(w1: np.ndarray, w3: np.ndarray, x64: np.ndarray) -> np.ndarray:
+    """h = silu(W1 x) * (W3 x) for each row x of x64, unrounded (float64).
+
+    w1 = gate_proj, w3 = up_proj ([PR1192] pre-stacked expert rename:
+    w1 -> gate_proj, w3 -> up_proj).
+    """
+    g = x64 @ w1.T
+    u = x64 @ w3.T
+    return silu(g) * u
+
+
 def swiglu_expert(w1: np.ndarray, w3: np.ndarray, w2: np.ndarray, x64: np.ndarray,
                   round_h: bool = True) -> np.ndarray:
     """y = W2 (silu(W1 x) * (W3 x)) for each row x of x64.
 
-    w1 = gate_proj, w3 = up_proj, w2 = down_proj ([PR1192] pre-stacked expert
-    rename: w1 -> gate_proj, w2 -> down_proj, w3 -> up_proj). The product h is
-    rounded to bf16 before the down projection when ``round_h`` (READING).
+    w2 = down_proj ([PR1192] pre-stacked expert rename: w2 -> down_proj). The
+    product h (swiglu_h) is rounded to bf16 before the down projection when
+    ``round_h`` (READING).
     """
-    g = x64 @ w1.T
-    u = x64 @ w3.T
-    h = silu(g) * u
+    h = swiglu_h(w1, w3, x64)
     if round_h:
         h = round_bf16(h)
     return h @ w2.T
 
 
-def _expert_mats(ew, e: int = 0):
+def expert_mats(ew, e: int = 0):
+    """Expert e of a set of SwiGLU weights as float64 (w1, w3, w2)."""
     return dequant(ew.gate, e), dequant(ew.up, e), dequant(ew.down, e)
 
 
@@ -380,12 +390,12 @@ def forward(layer, x_bits, token_ids=None, ids=None, round_h: bool = True):
     y_slot = np.zeros((T * k, d))
     for e in np.nonzero(counts)[0]:
         slots = perm[offsets[e]:offsets[e + 1]]
-        w1, w3, w2 = _expert_mats(layer.routed_expert(int(e)))
+        w1, w3, w2 = expert_mats(layer.routed_expert(int(e)))
         y_slot[slots] = swiglu_expert(w1, w3, w2, x[slots // k], round_h)
 
     y_sh = np.zeros((T, d))
     if layer.shared is not None:
-        w1, w3, w2 = _expert_mats(layer.shared)
+        w1, w3, w2 = expert_mats(layer.shared)
         y_sh = swiglu_expert(w1, w3, w2, x, round_h)
 
     y = np.zeros((T, d))
@@ -418,11 +428,11 @@ def forward_tokens(layer, x_bits, tokens, ids, round_h: bool = True, expert_cach
         for j in range(k):
             e = int(ids[i, j])
             if e not in cache:
-                cache[e] = _expert_mats(layer.routed_expert(e))
+                cache[e] = expert_mats(layer.routed_expert(e))
             y_slot[i, j] = swiglu_expert(*cache[e], x[i:i + 1], round_h)[0]
     y_sh = np.zeros((n, d))
     if layer.shared is not None:
-        y_sh = swiglu_expert(*_expert_mats(layer.shared), x, round_h)
+        y_sh = swiglu_expert(*expert_mats(layer.shared), x, round_h)
     y = np.einsum("nk,nkd->nd", w, y_slot) + y_sh
     return w, y_slot, y_sh, y
 

@@ -18,4 +18,5 @@ from .api import (  # noqa: F401
     route,
     router_logits,
     workspace_init,
+    ws_region,
 )

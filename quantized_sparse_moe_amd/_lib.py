@@ -52,10 +52,18 @@ class LayerC(Structure):
     _fields_ = [("router", RouterC), ("routed", ExpertsC), ("shared", POINTER(ExpertsC))]
 
 
+class WsLayoutC(Structure):
+    _fields_ = [("total", c_size_t), ("ids", c_size_t), ("weights", c_size_t), ("logits", c_size_t),
+                ("keys", c_size_t), ("scores", c_size_t), ("offsets", c_size_t), ("perm", c_size_t),
+                ("h", c_size_t), ("h_shared", c_size_t), ("y_slot", c_size_t), ("y_shared", c_size_t),
+                ("fused", c_int32)]
+
+
 # name -> (restype, argtypes)
 _SIGS = {
     "moe_workspace_size": (c_size_t, [POINTER(LayerC), c_int32]),
     "moe_workspace_init": (c_int32, [c_void_p, c_size_t, c_void_p]),
+    "moe_workspace_layout": (c_int32, [POINTER(LayerC), c_int32, POINTER(WsLayoutC)]),
     "moe_route": (c_int32, [POINTER(RouterC), c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,
                             c_void_p]),
     "moe_permute": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_size_t,

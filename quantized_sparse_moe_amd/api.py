@@ -137,6 +137,13 @@ class DeviceLayer:
         workspace_init(ws)
         return ws
 
+    def workspace_layout(self, T: int) -> dict:
+        """moe_workspace_layout: byte offsets of moe_forward's intermediates in
+        the workspace for T tokens (0: not written), plus 'total' and 'fused'."""
+        out = _lib.WsLayoutC()
+        check(_lib.load().moe_workspace_layout(ctypes.byref(self.c), T, ctypes.byref(out)), "moe_workspace_layout")
+        return {name: getattr(out, name) for name, _ in _lib.WsLayoutC._fields_}
+
 
 def workspace_init(ws: torch.Tensor, stream=None) -> None:
     check(_lib.load().moe_workspace_init(_ptr(ws), ws.numel(), _stream(stream)), "moe_workspace_init")
@@ -269,6 +276,18 @@ def forward_probed(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torc
                                          ws.numel(), _stream(stream), evs, n, names, ctypes.byref(count)),
           "moe_forward_probed")
     return [names[i].decode() for i in range(count.value)]
+
+
+def ws_region(ws: torch.Tensor, offset: int, dtype: torch.dtype, shape) -> torch.Tensor:
+    """A view of `shape` elements of `dtype` at byte `offset` of a workspace
+    (for reading the intermediates moe_workspace_layout locates)."""
+    n = 1
+    for s in shape:
+        n *= s
+    nbytes = n * torch.tensor([], dtype=dtype).element_size()
+    if offset <= 0 or offset + nbytes > ws.numel():
+        raise ValueError(f"region [{offset}, {offset + nbytes}) outside the workspace")
+    return ws[offset:offset + nbytes].view(dtype).view(*shape)
 
 
 @dataclass

@@ -145,20 +145,4 @@ __device__ __forceinline__ void set_device_error(int32_t* err, int code) {
   if (err) atomicOr(err, code);
 }
 
-// Optional phase timeline for performance analysis builds (-DQSMOE_TIMELINE):
-// thread 0 of a workgroup records the 100 MHz wall clock at a phase boundary.
-#ifdef QSMOE_TIMELINE
-constexpr int kTimelineRegion = 1 << 15;  // entries per kernel region
-extern __device__ uint64_t g_timeline[4 * kTimelineRegion];
-#define QSMOE_TL(region, slot)                                                                   \
-  do {                                                                                          \
-    if (threadIdx.x == 0 && blockIdx.x * 8 + (slot) < kTimelineRegion)                          \
-      g_timeline[(region) * kTimelineRegion + blockIdx.x * 8 + (slot)] = wall_clock64();        \
-  } while (0)
-#else
-#define QSMOE_TL(region, slot) \
-  do {                         \
-  } while (0)
-#endif
-
 }  // namespace qsmoe

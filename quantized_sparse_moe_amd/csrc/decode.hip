@@ -28,25 +28,8 @@
 
 namespace qsmoe {
 
-#ifdef QSMOE_TIMELINE
-__device__ uint64_t g_timeline[4 * kTimelineRegion];
-
-hipError_t timeline_copy(void* host, size_t bytes) {
-  hipError_t e = hipDeviceSynchronize();
-  if (e != hipSuccess) return e;
-  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), bytes, 0, hipMemcpyDeviceToHost);
-}
-#endif
-
-// Single-token launch 2 with one 512-thread workgroup per CU.
-#ifndef QSMOE_DEC_GU1
-#define QSMOE_DEC_GU1 1
-#endif
-
-
 constexpr int kDecMaxT = 4;
 constexpr int kDecMaxK = 8;
-
 
 // Launch 1: router logits of one expert per workgroup (split-K over its four
 // waves), with the expert's score and ranking key for every token; the
@@ -55,17 +38,14 @@ constexpr int kDecMaxK = 8;
 template <int TT, int SCPL, int SNT>
 __global__ __launch_bounds__(256) void k_dec_router(DecodeArgs a) {
   __shared__ float s_part[4 * TT];
-  QSMOE_TL(0, 0);
   if (static_cast<int>(blockIdx.x) < a.n_logit_blocks) {
     logits_wg<TT>(a.x, a.wr, a.T, a.E, a.d, blockIdx.x, 0, a.logits, s_part, a.bias, a.keys, a.scores);
-    QSMOE_TL(0, 1);
   } else if constexpr (SNT > 0) {
     StreamArgs sa{a.sgate, a.sup, a.x, a.T, a.k, 1, nullptr, nullptr, 1, a.h_sh, nullptr};
     ffn_stream_body<0, 8, SCPL, SNT, true>(sa, blockIdx.x - a.n_logit_blocks, gridDim.x - a.n_logit_blocks, nullptr,
                                            nullptr);
   }
   __syncthreads();
-  QSMOE_TL(0, 7);
 }
 
 // Hash route of token t by one wave (the pages' tid2eid table, as k_hash):
@@ -105,7 +85,6 @@ __device__ __forceinline__ void dec_hash_head(const DecodeArgs& a, int t, bool p
 template <int F, int B, int CPL>
 __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   __shared__ int32_t s_ids[kDecMaxT * kDecMaxK];
-  QSMOE_TL(1, 0);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   if (wave < a.T) {
     int id;
@@ -135,7 +114,6 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
     }
   }
   __syncthreads();
-  QSMOE_TL(1, 1);
   const int rows = a.gate.rows, nchunks = a.gate.cols >> 5;
   const int64_t total = static_cast<int64_t>(a.T) * a.k * rows;
   const int64_t W = static_cast<int64_t>(gridDim.x) * 4, gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
@@ -160,7 +138,6 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
     u += r_end - r_begin;
   }
   __syncthreads();
-  QSMOE_TL(1, 7);
 }
 
 // Launch 2 for a single token: one 512-thread workgroup per CU takes an equal
@@ -173,7 +150,6 @@ template <int F, int B, int CPL>
 __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   __shared__ int32_t s_ids[kDecMaxK];
   __shared__ uint32_t s_next;
-  QSMOE_TL(1, 0);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   if (wave == 0) {
     int id;
@@ -211,7 +187,6 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   XRaw<CPL, 1> xw;
   load_x_raw<CPL, 1>(xw, xrow, lane, nchunks);
   __syncthreads();
-  QSMOE_TL(1, 1);
   if (u_begin >= u_end) return;
   auto grab = [&]() -> uint32_t {
     uint32_t v = 0;
@@ -252,7 +227,6 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
       u0 = u2;
     }
   }
-  QSMOE_TL(1, 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -327,7 +301,6 @@ constexpr int kDecSegRows = 4;  // output rows per segment of a wave's range
 // its routed rows, one row ahead of the arithmetic.
 template <int F, int B, int K, bool SH>
 __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
-  QSMOE_TL(2, 0);
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int rows = a.down.rows, I = a.down.cols, nchunks = I >> 5;
   const int Ish = SH ? a.sdown.cols : 32, nchunks_sh = Ish >> 5;
@@ -384,7 +357,6 @@ __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
       dec_load_routed<F, B, K>(A, qd, min(seg0, r_end - 1), lane, nchunks);
       if constexpr (FIRST) {
         finish_x<F, B, 1, K>(hx, hw, hvalid, lane, nchunks);
-        QSMOE_TL(2, 1);
       }
       float ysh[kDecSegRows];
 #pragma unroll
@@ -404,7 +376,6 @@ __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
     u += r_end - r_begin;
   }
   __syncthreads();
-  QSMOE_TL(2, 7);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,25 +392,18 @@ bool decode_path_supported(const DecodeArgs& a) {
 }
 
 // Grid sizing of launches 2 and 3: at most kDecMaxWg workgroups, at least
-// the given rows per wave.
-#ifndef QSMOE_DEC_MAX_WG
-#define QSMOE_DEC_MAX_WG 512
-#endif
-#ifndef QSMOE_DEC_GU_MIN_ROWS
-#define QSMOE_DEC_GU_MIN_ROWS 2
-#endif
-#ifndef QSMOE_DEC_SH_MIN_ROWS
-#define QSMOE_DEC_SH_MIN_ROWS 2
-#endif
-#ifndef QSMOE_DEC_DN_MIN_ROWS
-#define QSMOE_DEC_DN_MIN_ROWS 4
-#endif
+// the given rows per wave (measured: 2 rows per wave for gate/up and the
+// shared gate/up, 4 for the down projection).
+constexpr int64_t kDecMaxWg = 512;
+constexpr int kDecGuMinRows = 2;
+constexpr int kDecShMinRows = 2;
+constexpr int kDecDnMinRows = 4;
 
 // Workgroups for `units` rows with at least `min_rows` rows per wave.
 static unsigned dec_grid(int64_t units, int min_rows = 2) {
   const int64_t per_wg = 4 * min_rows;
   return static_cast<unsigned>(
-      std::max<int64_t>(1, std::min<int64_t>((units + per_wg - 1) / per_wg, QSMOE_DEC_MAX_WG)));
+      std::max<int64_t>(1, std::min<int64_t>((units + per_wg - 1) / per_wg, kDecMaxWg)));
 }
 
 #define QSMOE_DEC_FMT(FMT_, BITS_, ...)                      \
@@ -477,7 +441,7 @@ hipError_t launch_dec_router(const DecodeArgs& a0, hipStream_t s) {
   const int scpl = a.has_shared ? dec_cpl(a.sgate.cols) : 1;
   const int snt = dec_shared_nt(a, scpl);
   unsigned grid = a.n_logit_blocks;
-  if (snt > 0) grid += dec_grid(static_cast<int64_t>((a.T + snt - 1) / snt) * a.sgate.rows, QSMOE_DEC_SH_MIN_ROWS);
+  if (snt > 0) grid += dec_grid(static_cast<int64_t>((a.T + snt - 1) / snt) * a.sgate.rows, kDecShMinRows);
   const int tt = a.T <= 1 ? 1 : (a.T <= 2 ? 2 : 4);
 #define QSMOE_K1(CP, NT_)                                                                   \
   do {                                                                                      \
@@ -511,7 +475,7 @@ static int device_cus() {
 hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
   const int cpl = dec_cpl(a.gate.cols);
   const int cus = device_cus();
-  if (QSMOE_DEC_GU1 && a.T == 1 && cus > 0 && cpl <= 2) {  // (hidden > 4096 would spill at 512 threads)
+  if (a.T == 1 && cus > 0 && cpl <= 2) {  // (hidden > 4096 would spill at 512 threads)
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(cus, static_cast<int64_t>(a.k) * a.gate.rows))), block(512);
     QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
       if (cpl == 1)
@@ -521,7 +485,7 @@ hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
     })
     return hipGetLastError();
   }
-  const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.k * a.gate.rows, QSMOE_DEC_GU_MIN_ROWS)), block(256);
+  const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.k * a.gate.rows, kDecGuMinRows)), block(256);
   QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
     if (cpl == 1)
       QSMOE_LAUNCH((k_dec_gateup<F, B, 1>), grid, block, 0, s, a);
@@ -534,7 +498,7 @@ hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.down.rows, QSMOE_DEC_DN_MIN_ROWS)), block(256);
+  const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.down.rows, kDecDnMinRows)), block(256);
   const size_t lds = 0;
   const int K = a.k <= 2 ? 2 : (a.k <= 4 ? 4 : (a.k <= 6 ? 6 : 8));
 #define QSMOE_K3(K_)                                                                                   \

@@ -13,47 +13,81 @@ namespace qsmoe {
 template <int FMT, int BITS>
 struct Codec;
 
-// The pair of bf16 values 128.0 (0x4300) as a vector register: with one
-// operand already in a VGPR, "(w >> n) & mask | k" compiles to a single
-// v_and_or_b32 (the mask takes the one scalar operand a VOP3 may read).
-__device__ __forceinline__ uint32_t bf16x2_128() {
-  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(0x43004300, 0xE4, 0xF, 0xF, false));
+// Affine b-bit codes (b <= 4) become exact bf16 values without a multiply:
+// with the exponent of 2^b and the code in the top b bits of the 7-bit
+// mantissa, the bits (0x3F80 + (b << 7)) | (q << (7 - b)) are the value
+// 2^b + q. The offset 2^b is the smallest that keeps integer steps, so the
+// sums the kernels form (x times 2^b + q, the offset removed through the
+// group's sum of x) carry the least cancellation: 16 + q for 4-bit codes
+// instead of 128 + q.
+template <int BITS>
+constexpr uint32_t kCodeBase = 0x3F80u + (static_cast<uint32_t>(BITS) << 7);  // bf16 bits of 2^BITS
+
+// The pair (2^b, 2^b) as a vector register: with one operand already in a
+// VGPR, "(w >> n) & mask | k" compiles to a single v_and_or_b32 (the mask
+// takes the one scalar operand a VOP3 may read).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_base_pair() {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(kCodeBase<BITS> * 0x10001u), 0xE4, 0xF,
+                                                        0xF, false));
+}
+
+// Code fields at bit `at` of each 16-bit half of w moved to the top BITS bits
+// of the bf16 mantissa (bit 7 - BITS), masked, with the exponent of 2^BITS.
+template <int BITS, int AT>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w, uint32_t k) {
+  constexpr int kTop = 7 - BITS;
+  constexpr uint32_t kMask = ((1u << BITS) - 1u) * 0x10001u << kTop;
+  if constexpr (AT >= kTop)
+    return ((w >> (AT - kTop)) & kMask) | k;
+  else
+    return ((w << (kTop - AT)) & kMask) | k;
 }
 
 // Affine 4-bit: word j holds codes 8j..8j+7; pair m = 4j + i is (8j+i, 8j+i+4).
 template <>
 struct Codec<0, 4> {
-  static constexpr float kOff = 128.0f;
+  static constexpr float kOff = 16.0f;
   static constexpr int lo(int m) { return 8 * (m >> 2) + (m & 3); }
   static constexpr int hi(int m) { return lo(m) + 4; }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[4], uint32_t (&p)[16]) {
-    const uint32_t k = bf16x2_128();
+    const uint32_t k = code_base_pair<4>();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[4 * j + i] = ((w[j] >> (4 * i)) & 0x000f000fu) | k;
+    for (int j = 0; j < 4; ++j) {
+      p[4 * j + 0] = code_pair<4, 0>(w[j], k);
+      p[4 * j + 1] = code_pair<4, 4>(w[j], k);
+      p[4 * j + 2] = code_pair<4, 8>(w[j], k);
+      p[4 * j + 3] = code_pair<4, 12>(w[j], k);
+    }
   }
 };
 
 // Affine 2-bit: word j holds codes 16j..16j+15; pair m = 8j + i is (16j+i, 16j+i+8).
 template <>
 struct Codec<0, 2> {
-  static constexpr float kOff = 128.0f;
+  static constexpr float kOff = 4.0f;
   static constexpr int lo(int m) { return 16 * (m >> 3) + (m & 7); }
   static constexpr int hi(int m) { return lo(m) + 8; }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[2], uint32_t (&p)[16]) {
-    const uint32_t k = bf16x2_128();
+    const uint32_t k = code_base_pair<2>();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[8 * j + i] = ((w[j] >> (2 * i)) & 0x00030003u) | k;
+    for (int j = 0; j < 2; ++j) {
+      p[8 * j + 0] = code_pair<2, 0>(w[j], k);
+      p[8 * j + 1] = code_pair<2, 2>(w[j], k);
+      p[8 * j + 2] = code_pair<2, 4>(w[j], k);
+      p[8 * j + 3] = code_pair<2, 6>(w[j], k);
+      p[8 * j + 4] = code_pair<2, 8>(w[j], k);
+      p[8 * j + 5] = code_pair<2, 10>(w[j], k);
+      p[8 * j + 6] = code_pair<2, 12>(w[j], k);
+      p[8 * j + 7] = code_pair<2, 14>(w[j], k);
+    }
   }
 };
 
 // Affine 3-bit: 32 codes in a 96-bit stream; pair m is (m, m+16).
 template <>
 struct Codec<0, 3> {
-  static constexpr float kOff = 128.0f;
+  static constexpr float kOff = 8.0f;
   static constexpr int lo(int m) { return m; }
   static constexpr int hi(int m) { return m + 16; }
   __device__ static __forceinline__ uint32_t code(const uint32_t (&w)[3], int c) {
@@ -62,9 +96,9 @@ struct Codec<0, 3> {
     return ((w[word] >> off) | (w[word + 1] << (32 - off))) & 7u;
   }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[3], uint32_t (&p)[16]) {
-    const uint32_t k = bf16x2_128();
+    const uint32_t k = code_base_pair<3>();
 #pragma unroll
-    for (int m = 0; m < 16; ++m) p[m] = code(w, m) | (code(w, m + 16) << 16) | k;
+    for (int m = 0; m < 16; ++m) p[m] = (code(w, m) << 4) | (code(w, m + 16) << 20) | k;
   }
 };
 

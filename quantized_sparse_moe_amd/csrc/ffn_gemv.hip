@@ -21,9 +21,9 @@
 // per lane per chunk covers a contiguous 1 KB of a 4-bit row per wave, and the
 // NT tokens' activations stay in registers for all rows, packed as bf16 pairs
 // in the order the codes are unpacked. Codes are turned into bf16
-// pairs with integer ops only (for b <= 4, bf16 bits 0x4300 | q are the exact
-// value 128 + q), dotted with v_dot2_f32_bf16 into fp32, and the group's
-// scale and bias are applied once per 32-code chunk:
+// pairs with integer ops only (for b <= 4 the exact value off + q with
+// off = 2^b, one shift and one and-or per pair), dotted with v_dot2_f32_bf16
+// into fp32, and the group's scale and bias are applied once per 32-code chunk:
 //   sum_i x_i (s q_i + b) = s * sum_i x_i (q_i + off) + (b - off * s) * sum_i x_i.
 // MXFP4 nibbles become exact bf16 with v_cvt_scalef32_pk_bf16_fp4 (scale 1),
 // and the chunk sum is multiplied by the e8m0 power of two in fp32.
@@ -45,14 +45,12 @@ bool gemv_supported(const QMat& m) {
 
 // Tokens handled per pass over the rows, from the mean bucket size (the
 // activations of NT tokens x CPL chunks are held in registers).
-#ifndef QSMOE_GEMV_MAX_NTC
-#define QSMOE_GEMV_MAX_NTC 8
-#endif
+constexpr int kGemvMaxTokenChunks = 8;  // NT * CPL activation chunks held in registers
 static int tokens_per_pass(int T, int k, int E, int cpl, int shared) {
   const int buckets = shared ? 1 : (T * k < E ? T * k : E);
   const int per = shared ? T : (T * k + buckets - 1) / buckets;
   int nt = per <= 1 ? 1 : (per <= 2 ? 2 : 4);
-  while (nt * cpl > QSMOE_GEMV_MAX_NTC) nt >>= 1;
+  while (nt * cpl > kGemvMaxTokenChunks) nt >>= 1;
   return nt;
 }
 

@@ -327,18 +327,11 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   }
 }
 
-#ifndef QSMOE_MXW_NW
-#define QSMOE_MXW_NW 4  // waves per workgroup in k_mfma_mxfp4_w (4: two workgroups per CU, or 8: one)
-#endif
-#ifndef QSMOE_MXW_PIN_LOADS
-#define QSMOE_MXW_PIN_LOADS 1
-#endif
-#ifndef QSMOE_MXW_DEEP
-#define QSMOE_MXW_DEEP 1  // 4-deep weight ring in k_mfma_mxfp4_w for tiles of under 4 token blocks
-#endif
-#ifndef QSMOE_MXFP4_SCS
-#define QSMOE_MXFP4_SCS 4  // most K steps per scale load in k_mfma_mxfp4_w (1, 2 or 4)
-#endif
+// waves per workgroup in k_mfma_mxfp4_w (4: two workgroups per CU; 8 waves
+// over 512 columns, one workgroup per CU, measured slower: 1000 -> 1025 us)
+constexpr int kMxwWaves = 4;
+// most K steps per scale load in k_mfma_mxfp4_w (1, 2 or 4)
+constexpr int kMxfp4ScaleSteps = 4;
 
 // ---------------------------------------------------------------------------
 // MXFP4 grouped GEMM on 32 x 32 tiles (V_MFMA_F32_32X32X16_BF16).
@@ -360,9 +353,9 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
 // cover them. Per pass a wave reads 4 activation fragments from LDS and
 // converts 2 weight fragments for 8 MFMAs of 32 x 32 x 16.
 template <bool GATEUP, int SCS>
-__global__ __launch_bounds__(64 * QSMOE_MXW_NW, 8 / QSMOE_MXW_NW) void k_mfma_mxfp4_w(MfmaArgs a) {
+__global__ __launch_bounds__(64 * kMxwWaves, 8 / kMxwWaves) void k_mfma_mxfp4_w(MfmaArgs a) {
   typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-  constexpr int NW = QSMOE_MXW_NW;
+  constexpr int NW = kMxwWaves;
   constexpr int MT = 128;
   constexpr int MTW = MT / 32;                   // 32-token tiles per wave
   constexpr int NTILE = (GATEUP ? 32 : 64) * NW;  // output rows per workgroup (per matrix)
@@ -512,12 +505,10 @@ __global__ __launch_bounds__(64 * QSMOE_MXW_NW, 8 / QSMOE_MXW_NW) void k_mfma_mx
         __builtin_amdgcn_sched_barrier(0);
         load_b(b_ld, kb);
       }
-#if QSMOE_MXW_PIN_LOADS
       // keep the next step's loads at the top of this one: left to itself the
       // scheduler sinks them behind most of the MFMAs, and the wait before
       // the barrier then exposes their latency
       __builtin_amdgcn_sched_barrier(0);
-#endif
       if constexpr (NMT > 0) {
         float sc[2][2];
 #pragma unroll
@@ -603,7 +594,7 @@ __global__ __launch_bounds__(64 * QSMOE_MXW_NW, 8 / QSMOE_MXW_NW) void k_mfma_mx
     }
   };
   using D2 = std::integral_constant<int, 2>;
-  using D4 = std::integral_constant<int, (SCS == 4 && QSMOE_MXW_DEEP) ? 4 : 2>;
+  using D4 = std::integral_constant<int, SCS == 4 ? 4 : 2>;
   switch (nmt) {
     case 4: kloop(std::integral_constant<int, 4>{}, D2{}); break;
     case 3: kloop(std::integral_constant<int, 3>{}, D2{}); break;
@@ -617,12 +608,13 @@ __global__ __launch_bounds__(64 * QSMOE_MXW_NW, 8 / QSMOE_MXW_NW) void k_mfma_mx
 // Affine b-bit experts, b in {2, 3, 4} (w = s q + b per group of G inputs,
 // fp16 s and b).
 //
-// Codes become exact bf16 without a multiply: the bits 0x4300 | q are the
-// value 128 + q. Each MFMA pass covers 32 consecutive inputs, so all of them
-// lie in one group per output row, and per group the kernel gets
-//   D[m][n] = sum_k x[m][k] (128 + q[n][k])   and   X[m] = sum_k x[m][k]
+// Codes become exact bf16 without a multiply: the code in the top bits of
+// the mantissa of 2^b gives the value off + q, off = 2^b (code_pair). Each
+// MFMA pass covers 32 consecutive inputs, so all of them lie in one group per
+// output row, and per group the kernel gets
+//   D[m][n] = sum_k x[m][k] (off + q[n][k])   and   X[m] = sum_k x[m][k]
 // (X from an extra MFMA against a B operand of ones), then adds
-//   s[n] D[m][n] + (b[n] - 128 s[n]) X[m]
+//   s[n] D[m][n] + (b[n] - off s[n]) X[m]
 // = sum_k x[m][k] (s[n] q[n][k] + b[n]) to the fp32 accumulator: exact
 // products, fp32 sums, the group's scale and bias applied once per group.
 //
@@ -653,7 +645,7 @@ __device__ __forceinline__ u32x4_t interleave_halves(const u32x4_t& v) {
 }
 
 // A chunk of 8 codes as the bf16 pairs (v_i, v_{i+4}), i = 0..3, where v is
-// 128 + q for 2-, 3- and 4-bit codes (chunk word: code i at bit BITS i, code
+// 2^b + q for 2-, 3- and 4-bit codes (chunk word: code i at bit BITS i, code
 // i + 4 at bit 16 + BITS i) and q itself for 8-bit codes (two words, code i
 // in byte i % 4 of word i / 4; the byte converts exactly to fp32, whose top
 // half is the exact bf16).
@@ -669,10 +661,10 @@ __device__ __forceinline__ bf16x8_t chunk_to_bf16x8(const uint32_t (&f)[BITS == 
     }
     return __builtin_bit_cast(bf16x8_t, r);
   } else {
-    constexpr uint32_t m = ((1u << BITS) - 1u) * 0x10001u;
-    const uint32_t k = bf16x2_128();
+    const uint32_t k = code_base_pair<BITS>();
     const uint32_t w = f[0];
-    const u32x4_t r{(w & m) | k, ((w >> BITS) & m) | k, ((w >> (2 * BITS)) & m) | k, ((w >> (3 * BITS)) & m) | k};
+    const u32x4_t r{code_pair<BITS, 0>(w, k), code_pair<BITS, BITS>(w, k), code_pair<BITS, 2 * BITS>(w, k),
+                    code_pair<BITS, 3 * BITS>(w, k)};
     return __builtin_bit_cast(bf16x8_t, r);
   }
 }
@@ -692,30 +684,14 @@ __device__ __forceinline__ bf16x8_t e4m3_chunk_to_bf16x8(const uint32_t (&f)[2])
 }
 
 constexpr int kAffRB = 4;  // 16-column blocks per wave (affine)
-#ifndef QSMOE_MXFP4_W
-#define QSMOE_MXFP4_W 1
-#endif
-#ifndef QSMOE_AFF_UNROLL
-#define QSMOE_AFF_UNROLL 8
-#endif
-#ifndef QSMOE_AFF_MINWG
-#define QSMOE_AFF_MINWG 2
-#endif
-#ifndef QSMOE_AFF_NT
-#define QSMOE_AFF_NT 1
-#endif
-#ifndef QSMOE_AFF_MINWG3_G64
-#define QSMOE_AFF_MINWG3_G64 1
-#endif
-
 
 // workgroups per CU the register budget is cut for: 3 (168 VGPRs) for the
 // 4-bit, 64-group, 16-token down projection, which needs only a few more
 // (measured: 304 -> 294 us at 512 tokens; the gate/up one spills more and
-// got slower, 626 -> 647 us), else QSMOE_AFF_MINWG
+// got slower, 626 -> 647 us), else 2
 template <bool GATEUP, int BITS, int G, int MT>
 constexpr int aff_min_wg() {
-  return (QSMOE_AFF_MINWG3_G64 && !GATEUP && BITS == 4 && G == 64 && MT == 16) ? 3 : QSMOE_AFF_MINWG;
+  return (!GATEUP && BITS == 4 && G == 64 && MT == 16) ? 3 : 2;
 }
 
 // FMT 0: affine codes as above; FMT 2: MXFP8 (BITS 8, G 32), E4M3 codes with
@@ -737,7 +713,7 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
   // weight macro steps: ROWB bytes of each of a wave's 64 rows
   constexpr int QW = BITS == 8 ? 2 : 1;         // words per 8-code chunk as read
-  constexpr float kOff = BITS == 8 ? 0.0f : 128.0f;  // value of code 0 as decoded
+  constexpr float kOff = BITS == 8 ? 0.0f : static_cast<float>(1 << BITS);  // value of code 0 as decoded
   constexpr int LPR = 8;                        // lanes per row in one load
   constexpr int BPL = BITS == 3 ? 12 : 16;      // bytes per lane in one load
   constexpr int ROWB = LPR * BPL;               // bytes per row per macro step
@@ -828,7 +804,7 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
         // projection, whose weights more m-tiles share, got slower, and so
         // did the MXFP4 GEMM, which re-reads each expert per 128 tokens)
         u32x4_t v;
-        if constexpr (GATEUP && QSMOE_AFF_NT)
+        if constexpr (GATEUP)
           v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
         else
           v = *reinterpret_cast<const u32x4_t*>(p);
@@ -1033,7 +1009,6 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
     load_a(a_reg0, min(ks_begin + 1, nsteps - 1) * kKT);
     lds_barrier();
     int ks = ks_begin;
-#if QSMOE_AFF_UNROLL == 8
     for (; ks + 8 <= ks_end; ks += 8) {
       step(ks, J0{}, a_reg1, a_reg0);
       step(ks + 1, J1{}, a_reg0, a_reg1);
@@ -1051,17 +1026,6 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
     if (ks + 4 < ks_end) step(ks + 4, J4{}, a_reg1, a_reg0);
     if (ks + 5 < ks_end) step(ks + 5, J5{}, a_reg0, a_reg1);
     if (ks + 6 < ks_end) step(ks + 6, J6{}, a_reg1, a_reg0);
-#else
-    for (; ks + 4 <= ks_end; ks += 4) {
-      step(ks, J0{}, a_reg1, a_reg0);
-      step(ks + 1, J1{}, a_reg0, a_reg1);
-      step(ks + 2, J2{}, a_reg1, a_reg0);
-      step(ks + 3, J3{}, a_reg0, a_reg1);
-    }
-    if (ks < ks_end) step(ks, J0{}, a_reg1, a_reg0);
-    if (ks + 1 < ks_end) step(ks + 1, J1{}, a_reg0, a_reg1);
-    if (ks + 2 < ks_end) step(ks + 2, J2{}, a_reg1, a_reg0);
-#endif
   };
   if constexpr (MB == 2) {
     if (valid_mb == 2)
@@ -1144,17 +1108,17 @@ static void launch_affine(const MfmaArgs& a, hipStream_t s) {
 template <bool GATEUP>
 static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   const QMat& m = a.m0;
-  constexpr int kMxwN = (GATEUP ? 32 : 64) * QSMOE_MXW_NW;  // k_mfma_mxfp4_w's rows per workgroup
-  if (m.fmt == 1 && QSMOE_MXFP4_W && m.rows % kMxwN == 0) {
+  constexpr int kMxwN = (GATEUP ? 32 : 64) * kMxwWaves;  // k_mfma_mxfp4_w's rows per workgroup
+  if (m.fmt == 1 && m.rows % kMxwN == 0) {
     const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
     const dim3 grid(mfma_grid(a.T, a.k, a.E, m.rows, kMxwN, 128));
     // scale loads of c steps (4 c bytes) need rows of whole chunks on aligned scale arrays
     auto chunks = [&](int c) {
-      return c <= QSMOE_MXFP4_SCS && m.cols % (c * kKT) == 0 &&
+      return c <= kMxfp4ScaleSteps && m.cols % (c * kKT) == 0 &&
              reinterpret_cast<uintptr_t>(a.m0.scales) % (4 * c) == 0 &&
              reinterpret_cast<uintptr_t>(a.m1.scales) % (4 * c) == 0;
     };
-    const dim3 block(64 * QSMOE_MXW_NW);
+    const dim3 block(64 * kMxwWaves);
     if (chunks(4))
       QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 4>), grid, block, lds, s, a);
     else if (chunks(2))

@@ -105,8 +105,20 @@ moe_status check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
-size_t route_ws_bytes(const moe_router& r, int T) {
-  return kHeader + (r.mode == MOE_ROUTE_TOPK ? align_up(static_cast<size_t>(T) * r.num_experts * 4) : 0);
+// moe_route's workspace in top-k mode: header | logits fp32 [T][E] | packed
+// keys uint64 [T][E] | scores fp32 [T][E] (each region 256-byte aligned).
+struct RouteLayout {
+  size_t logits, keys, scores, total;
+};
+
+RouteLayout route_layout(const moe_router& r, int T) {
+  const size_t te = static_cast<size_t>(T) * r.num_experts;
+  RouteLayout l{kHeader, 0, 0, kHeader};
+  if (r.mode != MOE_ROUTE_TOPK) return l;
+  l.keys = l.logits + align_up(te * 4);
+  l.scores = l.keys + align_up(te * 8);
+  l.total = l.scores + align_up(te * 4);
+  return l;
 }
 
 // fp32 partial sums of the shared expert's K-split projections, bounded for
@@ -132,8 +144,12 @@ size_t ffn_ws_bytes(const moe_experts& routed, const moe_experts* shared, int T,
 }
 
 struct FwdLayout {
-  size_t ids, w, logits, keys, offsets, perm, h, h_sh, sh_part, y_slot, y_sh, total;
+  size_t ids, w, logits, keys, scores, offsets, perm, h, h_sh, sh_part, y_slot, y_sh, total;
 };
+
+// The fused small-batch path takes at most this many tokens (the decode
+// kernels check the rest of their conditions themselves).
+constexpr int kSmallBatch = 4;
 
 FwdLayout forward_layout(const moe_layer& L, int T) {
   const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;
@@ -144,13 +160,18 @@ FwdLayout forward_layout(const moe_layer& L, int T) {
   o += align_up(tk * 4);
   f.w = o;
   o += align_up(tk * 4);
-  // logits: top-k routing, and hash routing on the small-batch path (whose
-  // launch 1 computes every expert's logit and score)
-  const bool small = T <= 4;
+  // logits, packed ranking keys and scores of every expert: top-k routing,
+  // and hash routing on the small-batch path (whose launch 1 computes every
+  // expert's logit and score)
+  const bool small = T <= kSmallBatch;
+  const bool all_experts = L.router.mode == MOE_ROUTE_TOPK || small;
+  const size_t te = static_cast<size_t>(T) * E;
   f.logits = o;
-  o += L.router.mode == MOE_ROUTE_TOPK || small ? align_up(static_cast<size_t>(T) * E * 4) : 0;
-  f.keys = o;  // small-batch path only (T <= 4): ranking keys and scores
-  o += small ? align_up(static_cast<size_t>(T) * E * 12) : 0;
+  o += all_experts ? align_up(te * 4) : 0;
+  f.keys = o;
+  o += all_experts ? align_up(te * 8) : 0;
+  f.scores = o;
+  o += all_experts ? align_up(te * 4) : 0;
   f.offsets = o;
   o += align_up((E + 1) * 4);
   f.perm = o;
@@ -214,7 +235,7 @@ P* at(void* ws, size_t off) {
 }
 
 moe_status run_route(const moe_router& r, const uint16_t* x, const int32_t* token_ids, int T, int32_t* ids,
-                     float* w, float* logits, int32_t* err, hipStream_t s) {
+                     float* w, float* logits, uint64_t* keys, float* scores, int32_t* err, hipStream_t s) {
   hipError_t e;
   if (r.mode == MOE_ROUTE_HASH) {
     e = mark(launch_router_hash(x, r.weight, token_ids, r.tid2eid, T, r.num_experts, r.top_k, r.hidden, r.vocab,
@@ -225,8 +246,9 @@ moe_status run_route(const moe_router& r, const uint16_t* x, const int32_t* toke
   if ((e = mark(launch_router_logits(x, r.weight, T, r.num_experts, r.hidden, logits, s), "router_logits", s)) !=
       hipSuccess)
     return MOE_ERR_HIP;
-  return hip_status(
-      mark(launch_router_topk(logits, r.bias, T, r.num_experts, r.top_k, r.routed_scale, ids, w, s), "router_topk", s));
+  return hip_status(mark(
+      launch_router_topk(logits, r.bias, T, r.num_experts, r.top_k, r.routed_scale, ids, w, keys, scores, s),
+      "router_topk", s));
 }
 
 bool mfma_worthwhile(const QMat& m, int T, int k, int E) {
@@ -333,7 +355,50 @@ moe_status moe_mhc_sinkhorn(const float* logits, int64_t T, int32_t n, int32_t i
 
 size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens) {
   if (max_tokens < 0 || check_layer(layer) != MOE_OK) return 0;
-  return forward_layout(*layer, max_tokens > 0 ? max_tokens : 1).total;
+  // Every region grows with T, but the small-batch regions of a hash layer
+  // exist only up to kSmallBatch tokens: the larger of the two layouts serves
+  // every T <= max_tokens.
+  const int mt = max_tokens > 0 ? max_tokens : 1;
+  return std::max(forward_layout(*layer, std::min(mt, kSmallBatch)).total, forward_layout(*layer, mt).total);
+}
+
+moe_status moe_workspace_layout(const moe_layer* layer, int32_t T, moe_ws_layout* out) {
+  if (out == nullptr || T < 1) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_layer(layer);
+  if (s != MOE_OK) return s;
+  const moe_layer& L = *layer;
+  const FwdLayout f = forward_layout(L, T);
+  const bool small = T <= kSmallBatch, all_experts = L.router.mode == MOE_ROUTE_TOPK || small;
+  DecodeArgs da{};
+  da.T = T;
+  da.d = L.router.hidden;
+  da.E = L.router.num_experts;
+  da.k = L.router.top_k;
+  da.gate = to_qmat(L.routed.gate);
+  da.up = to_qmat(L.routed.up);
+  da.down = to_qmat(L.routed.down);
+  da.has_shared = L.shared != nullptr;
+  if (L.shared) {
+    da.sgate = to_qmat(L.shared->gate);
+    da.sup = to_qmat(L.shared->up);
+    da.sdown = to_qmat(L.shared->down);
+  }
+  const bool fused = decode_path_supported(da);
+  *out = moe_ws_layout{};
+  out->total = f.total;
+  out->fused = fused ? 1 : 0;
+  out->ids = f.ids;
+  out->weights = f.w;
+  out->logits = all_experts ? f.logits : 0;
+  out->keys = all_experts ? f.keys : 0;
+  out->scores = all_experts ? f.scores : 0;
+  out->offsets = fused ? 0 : f.offsets;
+  out->perm = fused ? 0 : f.perm;
+  out->h = f.h;
+  out->h_shared = L.shared ? f.h_sh : 0;
+  out->y_slot = fused ? 0 : f.y_slot;
+  out->y_shared = L.shared && !fused ? f.y_sh : 0;
+  return MOE_OK;
 }
 
 moe_status moe_workspace_init(void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -363,10 +428,11 @@ moe_status moe_route(const moe_router* router, const uint16_t* x_bf16, const int
   if (x_bf16 == nullptr || topk_ids == nullptr || topk_w == nullptr) return MOE_ERR_INVALID_ARG;
   if (router->mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16)) return MOE_ERR_ALIGNMENT;
-  if (ws == nullptr || ws_bytes < route_ws_bytes(*router, T)) return MOE_ERR_WORKSPACE;
+  const RouteLayout rl = route_layout(*router, T);
+  if (ws == nullptr || ws_bytes < rl.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  return run_route(*router, x_bf16, token_ids, T, topk_ids, topk_w, at<float>(ws, kHeader), at<int32_t>(ws, 0),
-                   stream);
+  return run_route(*router, x_bf16, token_ids, T, topk_ids, topk_w, at<float>(ws, rl.logits),
+                   at<uint64_t>(ws, rl.keys), at<float>(ws, rl.scores), at<int32_t>(ws, 0), stream);
 }
 
 moe_status moe_permute(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,
@@ -422,21 +488,30 @@ moe_status moe_combine(const float* y_slot, const float* topk_w, const float* y_
   return hip_status(launch_combine(y_slot, topk_w, y_shared, T, k, d, out_dtype == MOE_OUT_F32, out, stream));
 }
 
-moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
-                       int32_t out_dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward's checks of everything but the workspace. T == 0 passes (the
+// caller returns MOE_OK without a launch).
+moe_status check_forward_args(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                              int32_t out_dtype, const void* out) {
   if (T < 0) return MOE_ERR_INVALID_ARG;
   moe_status s = check_layer(layer);
   if (s != MOE_OK) return s;
-  const moe_layer& L = *layer;
   if (out_dtype != MOE_OUT_BF16 && out_dtype != MOE_OUT_F32) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (x_bf16 == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
-  if (L.router.mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
+  if (layer->router.mode == MOE_ROUTE_HASH && token_ids == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned(x_bf16, 16) || !aligned(out, 16)) return MOE_ERR_ALIGNMENT;
-  if (ws == nullptr) return MOE_ERR_WORKSPACE;
-  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
-  const FwdLayout f = forward_layout(L, T);
-  if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// The launch sequence of one forward on a validated layer and a workspace of
+// at least f.total bytes.
+moe_status run_forward(const moe_layer& L, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                       int32_t out_dtype, void* out, void* ws, const FwdLayout& f, hipStream_t stream) {
+  moe_status s;
   const int k = L.router.top_k, E = L.router.num_experts, d = L.router.hidden;
   if (L.router.mode == MOE_ROUTE_TOPK || L.router.mode == MOE_ROUTE_HASH) {
     DecodeArgs da{};
@@ -455,7 +530,7 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
     da.bias = L.router.bias;
     da.logits = at<float>(ws, f.logits);
     da.keys = at<uint64_t>(ws, f.keys);
-    da.scores = reinterpret_cast<float*>(at<uint64_t>(ws, f.keys) + static_cast<size_t>(T) * E);
+    da.scores = at<float>(ws, f.scores);
     da.gate = to_qmat(L.routed.gate);
     da.up = to_qmat(L.routed.up);
     da.down = to_qmat(L.routed.down);
@@ -484,7 +559,8 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
   int32_t* perm = at<int32_t>(ws, f.perm);
   float* y_slot = at<float>(ws, f.y_slot);
   float* y_sh = L.shared ? at<float>(ws, f.y_sh) : nullptr;
-  if ((s = run_route(L.router, x_bf16, token_ids, T, ids, w, at<float>(ws, f.logits), err, stream)) != MOE_OK)
+  if ((s = run_route(L.router, x_bf16, token_ids, T, ids, w, at<float>(ws, f.logits), at<uint64_t>(ws, f.keys),
+                     at<float>(ws, f.scores), err, stream)) != MOE_OK)
     return s;
   if (mark(launch_permute(ids, T * k, E, offsets, perm, err, stream), "permute", stream) != hipSuccess)
     return MOE_ERR_HIP;
@@ -493,6 +569,21 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
     return s;
   return hip_status(
       mark(launch_combine(y_slot, w, y_sh, T, k, d, out_dtype == MOE_OUT_F32, out, stream), "combine", stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                       int32_t out_dtype, void* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status s = check_forward_args(layer, x_bf16, token_ids, T, out_dtype, out);
+  if (s != MOE_OK || T == 0) return s;
+  if (ws == nullptr) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
+  const FwdLayout f = forward_layout(*layer, T);
+  if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
+  return run_forward(*layer, x_bf16, token_ids, T, out_dtype, out, ws, f, stream);
 }
 
 moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
@@ -508,11 +599,6 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
   if (s == MOE_OK && p.overflow) return MOE_ERR_INVALID_ARG;
   return s;
 }
-
-#ifdef QSMOE_TIMELINE
-// Analysis builds only: copy the phase timeline to host memory.
-moe_status moe_debug_timeline(void* host, size_t bytes) { return hip_status(timeline_copy(host, bytes)); }
-#endif
 
 moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream) {
   if (ws == nullptr || code_out == nullptr) return MOE_ERR_INVALID_ARG;

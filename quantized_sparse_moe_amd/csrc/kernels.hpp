@@ -41,8 +41,10 @@ struct QMat {
 // Router ---------------------------------------------------------------------
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E, int d, float* logits,
                                 hipStream_t s);
+// keys / scores (nullable): every expert's packed ranking key and score, as
+// the small-batch path keeps them.
 hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k, float routed_scale,
-                              int32_t* ids, float* w, hipStream_t s);
+                              int32_t* ids, float* w, uint64_t* keys, float* scores, hipStream_t s);
 hipError_t launch_router_hash(const uint16_t* x, const float* wr, const int32_t* token_ids,
                               const int32_t* tid2eid, int T, int E, int k, int d, int vocab, float routed_scale,
                               int32_t* ids, float* w, int32_t* err, hipStream_t s);
@@ -135,10 +137,6 @@ hipError_t launch_mhc_sinkhorn(const float* logits, int64_t T, int n, int iters,
 
 // Workspace ------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
-
-#ifdef QSMOE_TIMELINE
-hipError_t timeline_copy(void* host, size_t bytes);
-#endif
 
 // Does a GEMV kernel exist for this projection shape/format?
 bool gemv_supported(const QMat& m);

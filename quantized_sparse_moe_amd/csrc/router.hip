@@ -198,11 +198,13 @@ __global__ __launch_bounds__(kLogitsWaves * 64) void k_logits_mfma_ksplit(const 
 }
 
 // ---------------------------------------------------------------------------
-// Top-k: one wave per token (keys staged in LDS, 12 bytes per expert).
+// Top-k: one wave per token (keys staged in LDS, 12 bytes per expert); every
+// expert's packed key and score also go to `keys` / `scores` when given.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, const float* __restrict__ bias,
                                               int T, int E, int k, float routed_scale, int32_t* __restrict__ ids,
-                                              float* __restrict__ w) {
+                                              float* __restrict__ w, uint64_t* __restrict__ keys,
+                                              float* __restrict__ scores) {
   extern __shared__ uint64_t lds_keys[];
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -211,7 +213,9 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   float* s_s = reinterpret_cast<float*>(lds_keys + static_cast<size_t>(4) * E) + static_cast<size_t>(wave) * E;
   int id;
   float wt;
-  topk_wave(logits + static_cast<size_t>(t) * E, bias, E, k, routed_scale, s_key, s_s, id, wt);
+  const size_t o = static_cast<size_t>(t) * E;
+  topk_wave(logits + o, bias, E, k, routed_scale, s_key, s_s, id, wt, keys ? keys + o : nullptr,
+            scores ? scores + o : nullptr);
   if (lane < k) {
     ids[static_cast<size_t>(t) * k + lane] = id;
     w[static_cast<size_t>(t) * k + lane] = wt;
@@ -317,12 +321,10 @@ __global__ __launch_bounds__(256) void k_hash(const uint16_t* __restrict__ x, co
 // Largest T for the K-split logits kernel (16 x 16 tiles, K over 16 waves);
 // above it the 64 x 64-tile kernel. Measured: T=512 29 vs 50 us, T=4096 215
 // vs 58 us.
-#ifndef QSMOE_LOGITS_KSPLIT_MAX_T
-#define QSMOE_LOGITS_KSPLIT_MAX_T 512
-#endif
+constexpr int kLogitsKsplitMaxT = 512;
 hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E, int d, float* logits,
                                 hipStream_t s) {
-  if (T > QSMOE_LOGITS_KSPLIT_MAX_T) {
+  if (T > kLogitsKsplitMaxT) {
     QSMOE_LAUNCH(k_logits_mfma<4>, dim3((E + 63) / 64, (T + 63) / 64), dim3(256), 0, s, x, wr, T, E, d,
                        logits);
   } else if (T > 16) {
@@ -339,9 +341,10 @@ hipError_t launch_router_logits(const uint16_t* x, const float* wr, int T, int E
 }
 
 hipError_t launch_router_topk(const float* logits, const float* bias, int T, int E, int k, float routed_scale,
-                              int32_t* ids, float* w, hipStream_t s) {
+                              int32_t* ids, float* w, uint64_t* keys, float* scores, hipStream_t s) {
   const size_t lds = static_cast<size_t>(4) * E * (sizeof(uint64_t) + sizeof(float));
-  QSMOE_LAUNCH(k_topk, dim3((T + 3) / 4), dim3(256), lds, s, logits, bias, T, E, k, routed_scale, ids, w);
+  QSMOE_LAUNCH(k_topk, dim3((T + 3) / 4), dim3(256), lds, s, logits, bias, T, E, k, routed_scale, ids, w, keys,
+               scores);
   return hipGetLastError();
 }
 

@@ -179,11 +179,19 @@ __device__ __forceinline__ void topk_rounds_reg(uint64_t (&key)[4], const float 
 }
 
 // Top-k of one token by one wave from its logits (scores and keys computed
-// here, staged in LDS: s_key E uint64, s_s E floats).
+// here, staged in LDS: s_key E uint64, s_s E floats; also stored to keys_t /
+// scores_t when those are given).
 __device__ __forceinline__ void topk_wave(const float* __restrict__ logits_t, const float* __restrict__ bias, int E,
                                           int k, float routed_scale, uint64_t* s_key, float* s_s, int& id_out,
-                                          float& w_out) {
-  for (int e = lane_id(); e < E; e += 64) score_key(logits_t[e], bias, e, s_s[e], s_key[e]);
+                                          float& w_out, uint64_t* __restrict__ keys_t = nullptr,
+                                          float* __restrict__ scores_t = nullptr) {
+  for (int e = lane_id(); e < E; e += 64) {
+    score_key(logits_t[e], bias, e, s_s[e], s_key[e]);
+    if (keys_t != nullptr) {
+      keys_t[e] = s_key[e];
+      scores_t[e] = s_s[e];
+    }
+  }
   topk_rounds(s_key, s_s, E, k, routed_scale, id_out, w_out);
 }
 

@@ -96,6 +96,58 @@ def test_workspace_size_accounts_for_buffers():
     assert lib.moe_workspace_size(ctypes.byref(bad), 64) == 0
 
 
+def _layout(L, T):
+    out = _lib.WsLayoutC()
+    st = qm.load().moe_workspace_layout(ctypes.byref(L), T, ctypes.byref(out))
+    return st, out
+
+
+@pytest.mark.parametrize("mode,E,k,shared", [(1, 1024, 2, False), (0, 1024, 2, False), (1, 16, 6, True),
+                                             (0, 256, 6, True)])
+def test_workspace_size_serves_every_smaller_token_count(mode, E, k, shared):
+    """moe_workspace_size never falls as max_tokens grows, and a workspace of
+    that size holds moe_forward's layout for every T <= max_tokens (hash
+    layers keep logits, keys and scores on the small-batch path only)."""
+    lib = qm.load()
+    L = make_layer(E=E, k=k, mode=mode, shared=shared)
+    sizes = [lib.moe_workspace_size(ctypes.byref(L), n) for n in range(1, 41)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])), sizes
+    for n in (1, 3, 4, 5, 8, 40):
+        for T in range(1, n + 1):
+            st, lay = _layout(L, T)
+            assert st == _lib.MOE_OK and 0 < lay.total <= sizes[n - 1], (n, T, lay.total, sizes[n - 1])
+
+
+def test_workspace_layout_regions():
+    """Regions are 256-byte aligned, inside the workspace and disjoint; the
+    small-batch path keeps no buckets or y_slot, the general path does."""
+    lib = qm.load()
+    for mode, shared, T in [(0, True, 1), (0, True, 3), (0, True, 40), (1, False, 2), (1, False, 9)]:
+        L = make_layer(E=16, k=2, mode=mode, shared=shared)
+        st, lay = _layout(L, T)
+        assert st == _lib.MOE_OK
+        E, k, d, I = 16, 2, 256, 128
+        sizes = {"ids": T * k * 4, "weights": T * k * 4, "logits": T * E * 4, "keys": T * E * 8,
+                 "scores": T * E * 4, "offsets": (E + 1) * 4, "perm": T * k * 4, "h": T * k * I * 2,
+                 "h_shared": T * I * 2, "y_slot": T * k * d * 4, "y_shared": T * d * 4}
+        spans = []
+        for name, size in sizes.items():
+            off = getattr(lay, name)
+            if off:
+                assert off % 256 == 0 and off + size <= lay.total, name
+                spans.append((off, off + size, name))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:])), spans
+        assert lay.fused == (1 if T <= 4 else 0)
+        present = {n for _, _, n in spans}
+        assert {"ids", "weights", "h"} <= present
+        assert ("y_slot" in present) == (not lay.fused) and ("perm" in present) == (not lay.fused)
+        assert ("keys" in present) == (mode == 0 or T <= 4)
+        assert ("h_shared" in present) == shared
+    assert _layout(make_layer(), 0)[0] == _lib.MOE_ERR_INVALID_ARG
+    assert _layout(make_layer(bits=5), 2)[0] == _lib.MOE_ERR_UNSUPPORTED
+
+
 def test_zero_tokens_is_ok_without_launch():
     assert fwd(make_layer(), T=0) == _lib.MOE_OK
 

@@ -83,6 +83,41 @@ def test_quantize_exact_and_near_ties(bits, group):
     assert np.array_equal(biases.view(np.uint16), rb.view(np.uint16))
 
 
+def _biased_tie_rows(bits, group, cols, B, s):
+    """Ties away from zero: min b = B s and max b + (2^b - 1) s make the scale
+    exactly s and the bias b, and w = s (B + k + 1/2) gives the quotient
+    k + 1/2 exactly; then one bf16 step either side of each tie. |B| up to 120
+    makes the fast path's |b / s| term the larger part of its threshold."""
+    levels = (1 << bits) - 1
+    ks = np.arange(min(levels, 128))
+    rows = []
+    for nudge in (0, 1, -1):
+        g = np.resize(s * (B + ks + 0.5), group).astype(np.float32)
+        g[0], g[1] = s * B, s * (B + levels)
+        b = f32_to_bf16_bits(g)
+        assert np.array_equal(oracle.bf16_bits_to_f64(b), g.astype(np.float64))   # exact in bf16
+        b = b.astype(np.int32)
+        b[2:] += nudge
+        rows.append(np.tile(b.astype(np.uint16), cols // group))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("bits,group,B,s", [(2, 32, 64, 2.0 ** -6), (3, 64, 100, 1.0), (4, 64, 64, 2.0 ** -5),
+                                            (4, 128, -120, 2.0 ** -3), (8, 128, -64, 2.0 ** -4)])
+def test_quantize_ties_with_a_nonzero_minimum(bits, group, B, s):
+    """Exact ties and their one-step neighbours in groups whose minimum (the
+    bias) is up to 120 scale steps from zero: codes, scales and biases equal the
+    oracle's correctly rounded division bit for bit."""
+    w = _biased_tie_rows(bits, group, 2 * group, B, s)
+    codes, scales, biases, err = _gpu_quant(w, bits, group)
+    rc, rs, rb = oracle.quantize_affine(w, bits, group)
+    assert err == 0
+    assert np.all(rs.astype(np.float64)[0] == s) and np.all(rb.astype(np.float64)[0] == B * s)
+    assert np.array_equal(codes, rc)
+    assert np.array_equal(scales.view(np.uint16), rs.view(np.uint16))
+    assert np.array_equal(biases.view(np.uint16), rb.view(np.uint16))
+
+
 def test_quantize_ragged_tail_and_one_row():
     """Chunk counts that leave the last workgroup partly empty, and a single row."""
     for rows, cols, bits, group in [(3, 4096 + 64, 4, 64), (1, 64, 2, 64), (257, 96, 3, 32)]:

@@ -191,6 +191,26 @@ def test_one_hot_extracts_column():
     check_one_hot_extracts_column()
 
 
+def check_swiglu_h_one_hot():
+    """swiglu_h of a one-hot input at column c is silu(W1[:, c]) * W3[:, c]
+    (a gate/up swap, a missing silu or a transposed operand fails), and it is
+    the unrounded product that swiglu_expert rounds to bf16 before W2."""
+    rng = np.random.default_rng(5)
+    w1, w3, w2 = rng.standard_normal((6, 8)), rng.standard_normal((6, 8)), rng.standard_normal((8, 6))
+    for c in (0, 5, 7):
+        x = np.zeros((1, 8))
+        x[0, c] = 1.0
+        h = oracle.swiglu_h(w1, w3, x)[0]
+        want = [w1[i, c] / (1.0 + math.exp(-w1[i, c])) * w3[i, c] for i in range(6)]
+        assert np.allclose(h, want, rtol=1e-14, atol=0)
+        y = oracle.swiglu_expert(w1, w3, w2, x)[0]
+        assert np.array_equal(y, oracle.round_bf16(h) @ w2.T)
+
+
+def test_swiglu_h_one_hot():
+    check_swiglu_h_one_hot()
+
+
 def check_zero_weights_give_zero():
     layer, _ = build_tiny_layer(41, shared=8)
     for ew in [layer.routed_expert(e) for e in range(layer.cfg.E)] + [layer.shared]:

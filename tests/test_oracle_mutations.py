@@ -162,6 +162,11 @@ def m_swiglu_transposed_down(w1, w3, w2, x64, round_h=True):
     return h @ w2.reshape(w2.shape[1], w2.shape[0])
 
 
+def m_swiglu_h_silu_on_up(w1, w3, x64):
+    """silu applied to the up projection instead of the gate."""
+    return (x64 @ w1.T) * om.silu(x64 @ w3.T)
+
+
 def m_round_via_fp32(v):
     return orig["round_bf16"](np.asarray(v, np.float64).astype(np.float32).astype(np.float64))
 
@@ -184,6 +189,7 @@ MUTATIONS = [
     ("permute", m_permute_reverse_in_bucket, [L.check_permute_stable_sort]),
     ("swiglu_expert", m_swiglu_swapped, [L.check_one_hot_extracts_column]),
     ("swiglu_expert", m_swiglu_transposed_down, [L.check_one_hot_extracts_column]),
+    ("swiglu_h", m_swiglu_h_silu_on_up, [L.check_swiglu_h_one_hot, L.check_one_hot_extracts_column]),
     ("round_bf16", m_round_via_fp32, [F.check_bf16_rounding]),
     ("route_hash", m_hash_sorted_ids, [R.check_hash_route_lookup]),
     ("quantize_affine", m_quant_levels_pow2, [Q.check_grid_roundtrip, Q.check_quant_bounds]),
