@@ -267,6 +267,26 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
                        int32_t T, int32_t out_dtype, void* out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches and results as moe_forward, with the workspace taken from a
+ * library-owned device array of 64 MiB instead of a caller buffer. Each GPU
+ * the library runs on holds its own copy of the array until the process ends;
+ * its address is resolved on the first call on each device. The caller still
+ * passes inputs and outputs (same rules as moe_forward). Every call on a GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller. The
+ * device error word is cleared at the start of each call and is not reported
+ * (out-of-range ids are still clamped in bounds). Allocates nothing, makes no
+ * hipMalloc/hipFree and no host synchronisation. Errors: as moe_forward, and
+ * MOE_ERR_WORKSPACE when moe_workspace_layout(layer, T).total exceeds the
+ * 64 MiB (e.g. T = 512 at hidden 4096, intermediate 2048, top-6 fits; the
+ * 4096-token prefill does not), before anything is launched.
+ */
+moe_status moe_forward_noalloc(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids,
+                               int32_t T, int32_t out_dtype, void* out, hipStream_t stream);
+
 /* Test and inspection helpers (not on the hot path). */
 
 /* Router logits only: logits fp32 [T][E] (top-k mode's first kernel). */

@@ -10,6 +10,7 @@ from .api import (  # noqa: F401
     device_error,
     expert_ffn,
     forward,
+    forward_noalloc,
     forward_probed,
     forward_staged,
     mhc_sinkhorn,

@@ -74,6 +74,7 @@ _SIGS = {
                               c_void_p]),
     "moe_forward": (c_int32, [POINTER(LayerC), c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_size_t,
                               c_void_p]),
+    "moe_forward_noalloc": (c_int32, [POINTER(LayerC), c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "moe_forward_probed": (c_int32, [POINTER(LayerC), c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
                                      c_size_t, c_void_p, POINTER(c_void_p), c_int32, POINTER(c_char_p),
                                      POINTER(c_int32)]),

@@ -259,6 +259,19 @@ def forward(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tenso
     return out
 
 
+def forward_noalloc(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tensor], out: torch.Tensor,
+                    stream=None) -> torch.Tensor:
+    """moe_forward_noalloc: moe_forward on the library's own per-GPU workspace
+    (no workspace argument; calls on one GPU must not overlap in time). The
+    output type follows `out` (float32 or bfloat16)."""
+    x = _bits_tensor(x)
+    f32 = out.dtype == torch.float32
+    check(_lib.load().moe_forward_noalloc(ctypes.byref(layer.c), _ptr(x), _ptr(token_ids), x.shape[0],
+                                          _lib.MOE_OUT_F32 if f32 else _lib.MOE_OUT_BF16, _ptr(out),
+                                          _stream(stream)), "moe_forward_noalloc")
+    return out
+
+
 def forward_probed(layer: DeviceLayer, x: torch.Tensor, token_ids: Optional[torch.Tensor], out: torch.Tensor,
                    ws: torch.Tensor, events, stream=None):
     """moe_forward with a (start, stop) event pair per kernel, timestamped by

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "qsmoe.h"
 #include "kernels.hpp"
@@ -571,6 +572,28 @@ moe_status run_forward(const moe_layer& L, const uint16_t* x_bf16, const int32_t
       mark(launch_combine(y_slot, w, y_sh, T, k, d, out_dtype == MOE_OUT_F32, out, stream), "combine", stream));
 }
 
+// The allocation-free variant's workspace: one array per GPU, resolved to its
+// device address once per device (hipGetSymbolAddress with that device
+// current); host code uses only the resolved address.
+constexpr size_t kStaticScratchBytes = size_t{64} << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status static_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -583,6 +606,20 @@ moe_status moe_forward(const moe_layer* layer, const uint16_t* x_bf16, const int
   if (!aligned(ws, 256)) return MOE_ERR_ALIGNMENT;
   const FwdLayout f = forward_layout(*layer, T);
   if (ws_bytes < f.total) return MOE_ERR_WORKSPACE;
+  return run_forward(*layer, x_bf16, token_ids, T, out_dtype, out, ws, f, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_layer* layer, const uint16_t* x_bf16, const int32_t* token_ids, int32_t T,
+                               int32_t out_dtype, void* out, hipStream_t stream) {
+  moe_status s = check_forward_args(layer, x_bf16, token_ids, T, out_dtype, out);
+  if (s != MOE_OK || T == 0) return s;
+  const FwdLayout f = forward_layout(*layer, T);
+  if (f.total > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((s = static_scratch(&ws)) != MOE_OK) return s;
+  // the sticky error word starts each call at zero (a kernel, not a memset)
+  if (launch_fill_i32(static_cast<int32_t*>(ws), 0, static_cast<int>(kHeader / 4), stream) != hipSuccess)
+    return MOE_ERR_HIP;
   return run_forward(*layer, x_bf16, token_ids, T, out_dtype, out, ws, f, stream);
 }
 
