@@ -306,6 +306,25 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
                               hipStream_t stream, hipEvent_t* events, int32_t n_events, const char** names,
                               int32_t* n_kernels);
 
+/* Measurement kernels (not part of the layer): the scale for HBM byte
+ * counters and the achievable rates beside the nominal peaks.
+ * moe_probe_stream: mode 0 reads every byte of buf [bytes] once (16 bytes per
+ * lane, consecutive lanes on consecutive pieces: bytes of traffic); mode 1
+ * reads the first 32 bytes of every 128-byte line (bytes / 4 requested);
+ * mode 2 writes every byte once (bytes written). Modes 0 and 1 XOR every word
+ * read into *sink (device uint32, initialised by the caller). bytes > 0 and a
+ * multiple of 128; buf 16-byte aligned. Errors: INVALID_ARG, ALIGNMENT, HIP. */
+moe_status moe_probe_stream(void* buf, size_t bytes, int32_t mode, uint32_t* sink, hipStream_t stream);
+
+/* moe_probe_mfma: `workgroups` workgroups of 4 waves, each wave `iters` rounds
+ * of 8 independent V_MFMA_F32_32X32X16_BF16 (2 * 32 * 32 * 16 flops each), no
+ * memory traffic. out: device uint64 [5], out[4] zeroed by the caller; wave 0
+ * of workgroup 0 writes its shader-clock counter (s_memtime) before and after
+ * its loop to out[0], out[1] and the 100 MHz wall clock to out[2], out[3]:
+ * the sustained shader clock is (out[1] - out[0]) / ((out[3] - out[2]) / 1e8).
+ * Errors: INVALID_ARG, ALIGNMENT, HIP. */
+moe_status moe_probe_mfma(int32_t workgroups, int32_t iters, uint64_t* out, hipStream_t stream);
+
 /* Synchronises `stream`, then copies the workspace error word to *code_out. */
 moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream);
 

@@ -15,6 +15,8 @@ from .api import (  # noqa: F401
     forward_staged,
     mhc_sinkhorn,
     permute,
+    probe_mfma,
+    probe_stream,
     quantize_affine,
     route,
     router_logits,

@@ -80,6 +80,8 @@ _SIGS = {
                                      POINTER(c_int32)]),
     "moe_router_logits": (c_int32, [POINTER(RouterC), c_void_p, c_int32, c_void_p, c_void_p]),
     "moe_device_error": (c_int32, [c_void_p, POINTER(c_int32), c_void_p]),
+    "moe_probe_stream": (c_int32, [c_void_p, c_size_t, c_int32, c_void_p, c_void_p]),
+    "moe_probe_mfma": (c_int32, [c_int32, c_int32, c_void_p, c_void_p]),
     "moe_mhc_sinkhorn": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_float, c_void_p, c_void_p]),
     "moe_quantize_affine": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p]),

@@ -303,6 +303,18 @@ def ws_region(ws: torch.Tensor, offset: int, dtype: torch.dtype, shape) -> torch
     return ws[offset:offset + nbytes].view(dtype).view(*shape)
 
 
+def probe_stream(buf: torch.Tensor, mode: int, sink: Optional[torch.Tensor] = None, stream=None) -> None:
+    """moe_probe_stream over all of `buf` (a contiguous device tensor):
+    mode 0 dense read, 1 the first 32 bytes of every 128-byte line, 2 write."""
+    check(_lib.load().moe_probe_stream(_ptr(buf), buf.numel() * buf.element_size(), mode, _ptr(sink),
+                                       _stream(stream)), "moe_probe_stream")
+
+
+def probe_mfma(workgroups: int, iters: int, out: torch.Tensor, stream=None) -> None:
+    """moe_probe_mfma into `out` (int64 [5] on the device, zeroed by the caller)."""
+    check(_lib.load().moe_probe_mfma(workgroups, iters, _ptr(out), _stream(stream)), "moe_probe_mfma")
+
+
 @dataclass
 class Intermediates:
     ids: torch.Tensor

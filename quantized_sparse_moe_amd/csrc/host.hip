@@ -637,6 +637,19 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
   return s;
 }
 
+moe_status moe_probe_stream(void* buf, size_t bytes, int32_t mode, uint32_t* sink, hipStream_t stream) {
+  if (buf == nullptr || bytes == 0 || bytes % 128 != 0 || mode < 0 || mode > 2) return MOE_ERR_INVALID_ARG;
+  if (mode != 2 && sink == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(buf, 16) || (sink != nullptr && !aligned(sink, 4))) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_probe_stream(buf, bytes, mode, sink, stream));
+}
+
+moe_status moe_probe_mfma(int32_t workgroups, int32_t iters, uint64_t* out, hipStream_t stream) {
+  if (workgroups < 1 || iters < 1 || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(out, 8)) return MOE_ERR_ALIGNMENT;
+  return hip_status(launch_probe_mfma(workgroups, iters, out, stream));
+}
+
 moe_status moe_device_error(const void* ws, int32_t* code_out, hipStream_t stream) {
   if (ws == nullptr || code_out == nullptr) return MOE_ERR_INVALID_ARG;
   if (hipStreamSynchronize(stream) != hipSuccess) return MOE_ERR_HIP;

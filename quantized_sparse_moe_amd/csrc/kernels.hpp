@@ -135,6 +135,12 @@ hipError_t launch_quantize_affine(const uint16_t* w, int64_t rows, int cols, int
 hipError_t launch_mhc_sinkhorn(const float* logits, int64_t T, int n, int iters, float eps, float* out,
                                hipStream_t s);
 
+// Measurement kernels -----------------------------------------------------------
+// mode 0: read every byte of buf once (16 bytes per lane); 1: read the first
+// 32 bytes of every 128-byte line; 2: write every byte once.
+hipError_t launch_probe_stream(const void* buf, size_t bytes, int mode, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(int workgroups, int iters, uint64_t* out, hipStream_t s);
+
 // Workspace ------------------------------------------------------------------
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int n, hipStream_t s);
 

@@ -234,3 +234,16 @@ def test_mhc_sinkhorn_validates_before_launch():
     assert s(None, 0, 4, 10, 0.0, None, None) == _lib.MOE_OK                 # nothing to do
     assert s(None, 8, 4, 10, 0.0, F, None) == _lib.MOE_ERR_INVALID_ARG
     assert s(F + 2, 8, 4, 10, 0.0, F, None) == _lib.MOE_ERR_ALIGNMENT
+
+
+def test_probe_entry_points_validate():
+    lib = _lib.load()
+    F = 4096
+    assert lib.moe_probe_stream(None, 1024, 0, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_probe_stream(F, 1000, 0, F, None) == _lib.MOE_ERR_INVALID_ARG     # not a multiple of 128
+    assert lib.moe_probe_stream(F, 1024, 3, F, None) == _lib.MOE_ERR_INVALID_ARG     # mode
+    assert lib.moe_probe_stream(F, 1024, 0, None, None) == _lib.MOE_ERR_INVALID_ARG  # read needs a sink
+    assert lib.moe_probe_stream(F + 8, 1024, 2, None, None) == _lib.MOE_ERR_ALIGNMENT
+    assert lib.moe_probe_mfma(0, 10, F, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_probe_mfma(4, 10, None, None) == _lib.MOE_ERR_INVALID_ARG
+    assert lib.moe_probe_mfma(4, 10, F + 4, None) == _lib.MOE_ERR_ALIGNMENT

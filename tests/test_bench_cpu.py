@@ -74,16 +74,74 @@ def test_mfma_flops_and_bound_choice():
         assert (fl / (bench.MFMA_BF16_PEAK_TFLOPS * 1e12) >= by / (bench.HBM_PEAK_GBS * 1e9)) == mfma
 
 
-def test_stored_traffic_needs_the_same_sources(tmp_path, monkeypatch):
+def _write_counter_csv(path, rows):
+    """A rocprofv3 counter-collection CSV: one row per (dispatch, counter)."""
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w") as f:
+        f.write("Correlation_Id,Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for disp, kernel, counters in rows:
+            for name, v in counters.items():
+                f.write(f'{disp},{disp},"{kernel}",{name},{v}\n')
+
+
+def _counters_for(read_bytes, write_bytes, req=128):
+    """Counter values of a dispatch that reads/writes the given bytes in
+    requests of `req` bytes (128, 64 or 32), as the formulas read them."""
+    n = read_bytes // req
+    return ({"TCC_EA0_RDREQ_sum": n, "TCC_EA0_RDREQ_32B_sum": n if req == 32 else 0,
+             "TCC_BUBBLE_sum": n if req == 128 else 0, "TCC_EA0_RDREQ_DRAM_32B_sum": read_bytes // 32},
+            {"TCC_EA0_WRREQ_sum": write_bytes // 64, "TCC_EA0_WRREQ_64B_sum": write_bytes // 64,
+             "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum": write_bytes // 32, "TCC_EA0_RDREQ_DRAM_sum": n})
+
+
+def test_counter_ingestion_calibrates_and_records(tmp_path, monkeypatch):
+    """Ingestion checks the byte formulas on the three streams of known
+    traffic, then records every kernel's bytes per launch keyed by the label
+    moe_forward_probed gives it; the readings serve only the same sources."""
     prof = tmp_path / "profiles"
     prof.mkdir()
-    rec = {"decode": {"kernel": "dec_gateup", "fetch_kib": 1000.0, "write_kib": 10.0, "fetch_scale": 2.0,
-                      "write_scale": 1.0, "source_hash": bench.source_hash()}}
-    (prof / "hbm_traffic.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "source_hash", lambda: rec["decode"]["source_hash"])
-    assert bench.measured_traffic("decode", "dec_gateup") == 1000 * 1024 * 2 + 10 * 1024
-    assert bench.measured_traffic("decode", "dec_down_combine") is None
-    assert bench.measured_traffic("prefill", "routed_gateup_mfma") is None
+    monkeypatch.setattr(bench, "TRAFFIC_PATH", str(prof / "hbm_traffic.json"))
+    monkeypatch.setattr(bench, "source_hash", lambda: "sources-of-this-run")
+    C = bench.CAL_BYTES
+    # the 32-of-128-byte stream moves whole lines at DRAM (its 32-byte requests become 128-byte fetches)
+    streams = [("void qsmoe::k_probe_read<0>(unsigned int const*, unsigned long, unsigned int*)", C, 0, 128),
+               ("void qsmoe::k_probe_read<1>(unsigned int const*, unsigned long, unsigned int*)", C, 0, 128),
+               ("void qsmoe::k_probe_write(unsigned int*, unsigned long)", 0, C, 128)]
+    kernels = [("void qsmoe::k_dec_gateup1<0, 4, 2>(qsmoe::DecodeArgs)", 60_000_000, 30_000, 128),
+               ("void qsmoe::k_dec_down_combine<0, 4, 6, true>(qsmoe::DecodeArgs)", 38_000_000, 16_384, 64)]
+    for run, rows in (("calibrate", streams), ("decode", kernels)):
+        for p_, idx in (("_p1", 0), ("_p2", 1)):
+            _write_counter_csv(tmp_path / "out" / (run + p_) / "host" / "run_counter_collection.csv",
+                               [(d, k, _counters_for(r, w, q)[idx]) for d, (k, r, w, q) in enumerate(rows)])
+    bench.ingest_counters(str(tmp_path / "out"))
+    rec = json.loads((prof / "hbm_traffic.json").read_text())
+    assert rec["validated"] and rec["read_formula_max_error"] <= 0.05
+    dec = rec["workloads"]["decode"]
+    assert set(dec) == {"k_dec_gateup1<0, 4, 2>", "k_dec_down_combine<0, 4, 6, true>"}
+    g = dec["k_dec_gateup1<0, 4, 2>"]
+    assert abs(g["read_bytes"] - 60_000_000) < 128
+    assert (prof / "hbm_traffic.md").exists()
+    cfg = synth.config("decode")
+    assert bench.measured_traffic("decode", "dec_gateup", cfg) == g["read_bytes"] + g["write_bytes"]
+    assert bench.measured_traffic("decode", "dec_router", cfg) is None
     monkeypatch.setattr(bench, "source_hash", lambda: "changed")
-    assert bench.measured_traffic("decode", "dec_gateup") is None
+    assert bench.measured_traffic("decode", "dec_gateup", cfg) is None
+
+
+def test_rocprof_names_match_probe_labels_by_format():
+    """The routed experts' kernel, not the shared expert's, answers for a label."""
+    key = bench.kernel_key
+    assert key("void qsmoe::k_mfma_affine<true, 2, 128, 16, 0>(qsmoe::MfmaArgs)") == "k_mfma_affine<true, 2, 128, 16, 0>"
+    assert key("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<int>>(int, ...)") is None
+    mixed, prefill, mx8 = synth.config("mixed"), synth.config("prefill"), synth.config("mxfp8")
+    m = bench.kernel_matches
+    assert m("routed_gateup_mfma", mixed, "k_mfma_affine<true, 2, 128, 16, 0>")
+    assert not m("routed_gateup_mfma", mixed, "k_mfma_affine<true, 8, 64, 16, 0>")     # the shared expert
+    assert m("routed_down_mfma", mixed, "k_mfma_affine<false, 3, 128, 16, 0>")
+    assert m("routed_gateup_mfma", prefill, "k_mfma_mxfp4_w<true, 4>")
+    assert not m("routed_gateup_mfma", prefill, "k_mfma_mxfp4_w<false, 4>")
+    assert m("routed_down_mfma", mx8, "k_mfma_affine<false, 8, 32, 16, 2>")
+    assert m("routed_gateup", mixed, "k_ffn_stream<0, 2, 2, 1, true>")
+    assert not m("routed_gateup", mixed, "k_ffn_stream<0, 8, 2, 1, true>")
+    assert m("dec_gateup", mixed, "k_dec_gateup1<0, 2, 2>") and m("dec_router", mixed, "k_dec_router<1, 2, 1>")
