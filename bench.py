@@ -357,7 +357,7 @@ def calibrate():
     import quantized_sparse_moe_amd as qm
     qm.load()
     buf = torch.empty(CAL_BYTES // 4, dtype=torch.int32, device="cuda")
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
     for _ in range(3):
         qm.probe_stream(buf, 2)
         qm.probe_stream(buf, 0, sink)
@@ -399,7 +399,7 @@ def context_info():
     info = {"gpu": props.name, "compute_units": cus, "cpu_model": cpu_model(),
             "host_cpus": len(os.sched_getaffinity(0))}
     buf = torch.empty(1 << 30, dtype=torch.int32, device="cuda")          # 4 GiB
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
     qm.probe_stream(buf, 0, sink)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
     for a, b in ev:

@@ -311,9 +311,11 @@ moe_status moe_forward_probed(const moe_layer* layer, const uint16_t* x_bf16, co
  * moe_probe_stream: mode 0 reads every byte of buf [bytes] once (16 bytes per
  * lane, consecutive lanes on consecutive pieces: bytes of traffic); mode 1
  * reads the first 32 bytes of every 128-byte line (bytes / 4 requested);
- * mode 2 writes every byte once (bytes written). Modes 0 and 1 XOR every word
- * read into *sink (device uint32, initialised by the caller). bytes > 0 and a
- * multiple of 128; buf 16-byte aligned. Errors: INVALID_ARG, ALIGNMENT, HIP. */
+ * mode 2 writes every byte once (bytes written). Modes 0 and 1 run 2048
+ * workgroups; workgroup i stores the XOR of the words it read into sink[i]
+ * (device uint32 [2048], overwritten), so the XOR of the 2048 words is that
+ * of every word read. bytes > 0 and a multiple of 128; buf 16-byte aligned.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP. */
 moe_status moe_probe_stream(void* buf, size_t bytes, int32_t mode, uint32_t* sink, hipStream_t stream);
 
 /* moe_probe_mfma: `workgroups` workgroups of 4 waves, each wave `iters` rounds

@@ -305,7 +305,8 @@ def ws_region(ws: torch.Tensor, offset: int, dtype: torch.dtype, shape) -> torch
 
 def probe_stream(buf: torch.Tensor, mode: int, sink: Optional[torch.Tensor] = None, stream=None) -> None:
     """moe_probe_stream over all of `buf` (a contiguous device tensor):
-    mode 0 dense read, 1 the first 32 bytes of every 128-byte line, 2 write."""
+    mode 0 dense read, 1 the first 32 bytes of every 128-byte line, 2 write.
+    Reads need `sink`: 2048 int32 words on the device (one per workgroup)."""
     check(_lib.load().moe_probe_stream(_ptr(buf), buf.numel() * buf.element_size(), mode, _ptr(sink),
                                        _stream(stream)), "moe_probe_stream")
 

@@ -23,13 +23,9 @@
 #include <algorithm>
 #include <type_traits>
 
-#include "ffn_core.hpp"
-#include "router_core.hpp"
+#include "decode_core.hpp"
 
 namespace qsmoe {
-
-constexpr int kDecMaxT = 4;
-constexpr int kDecMaxK = 8;
 
 // Launch 1: router logits of one expert per workgroup (split-K over its four
 // waves), with the expert's score and ranking key for every token; the
@@ -48,34 +44,6 @@ __global__ __launch_bounds__(256) void k_dec_router(DecodeArgs a) {
   __syncthreads();
 }
 
-// Hash route of token t by one wave (the pages' tid2eid table, as k_hash):
-// lane j < k takes expert tid2eid[token][j]; the weights are the launch-1
-// scores of those experts renormalised over the k slots (summed in slot
-// order). A token id or table entry out of range sets the device error word
-// (publish: one workgroup only), the id becomes 0 and the token's weights 0.
-__device__ __forceinline__ void dec_hash_head(const DecodeArgs& a, int t, bool publish, int& id, float& wt) {
-  const int lane = lane_id();
-  int tok = a.token_ids[t];
-  bool ok = true;
-  if (tok < 0 || tok >= a.vocab) {
-    if (publish && lane == 0) set_device_error(a.err, 1);
-    tok = 0;
-    ok = false;
-  }
-  int e = lane < a.k ? a.tid2eid[static_cast<size_t>(tok) * a.k + lane] : 0;
-  const bool bad = lane < a.k && (e < 0 || e >= a.E);
-  if (__ballot(bad) != 0) {
-    if (publish && lane == 0) set_device_error(a.err, 2);
-    ok = false;
-  }
-  e = (bad || lane >= a.k) ? 0 : e;
-  const float s = lane < a.k ? a.scores[static_cast<size_t>(t) * a.E + e] : 0.0f;
-  float total = 0.0f;
-  for (int j = 0; j < a.k; ++j) total += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), j));
-  id = e;
-  wt = ok ? (total > 0.0f ? s / total : 1.0f / static_cast<float>(a.k)) * a.routed_scale : 0.0f;
-}
-
 // ---------------------------------------------------------------------------
 // Launch 2. Every workgroup first selects each token's top-k from the
 // launch-1 keys (wave t: token t, keys in registers; same selection as
@@ -89,22 +57,7 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   if (wave < a.T) {
     int id;
     float wt;
-    if (a.hash) {
-      dec_hash_head(a, wave, blockIdx.x == 0, id, wt);
-    } else {
-      uint64_t key[4];
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        const bool ok = e < a.E;
-        const size_t o = static_cast<size_t>(wave) * a.E + (ok ? e : 0);
-        key[i] = a.keys[o];
-        sc[i] = a.scores[o];
-        key[i] = ok ? key[i] : 0;
-      }
-      topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
-    }
+    dec_token_head(a, wave, blockIdx.x == 0, id, wt);
     if (lane < a.k) {
       s_ids[wave * a.k + lane] = id;
       if (blockIdx.x == 0) {
@@ -146,7 +99,9 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
 // row is computed. Two waves share each SIMD and the older one is issued
 // first: with a fixed split per wave (or per workgroup, two per CU) the
 // younger half measured ~20 % slower and the launch ended with it.
-template <int F, int B, int CPL>
+// FULL: the input width is exactly 64 CPL chunks of 32 (every lane's
+// chunks exist): validity masks and address clamps fold away.
+template <int F, int B, int CPL, bool FULL>
 __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   __shared__ int32_t s_ids[kDecMaxK];
   __shared__ uint32_t s_next;
@@ -154,21 +109,7 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   if (wave == 0) {
     int id;
     float wt;
-    if (a.hash) {
-      dec_hash_head(a, 0, blockIdx.x == 0, id, wt);
-    } else {
-      uint64_t key[4];
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        const bool ok = e < a.E;
-        key[i] = a.keys[ok ? e : 0];
-        sc[i] = a.scores[ok ? e : 0];
-        key[i] = ok ? key[i] : 0;
-      }
-      topk_rounds_reg(key, sc, a.k, a.routed_scale, id, wt);
-    }
+    dec_token_head(a, 0, blockIdx.x == 0, id, wt);
     if (lane < a.k) {
       s_ids[lane] = id;
       if (blockIdx.x == 0) {
@@ -177,7 +118,7 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
       }
     }
   }
-  const int rows = a.gate.rows, nchunks = a.gate.cols >> 5;
+  const int rows = a.gate.rows, nchunks = FULL ? 64 * CPL : a.gate.cols >> 5;
   const uint32_t total = static_cast<uint32_t>(a.k) * rows;
   const uint32_t u_begin = static_cast<uint32_t>(static_cast<uint64_t>(total) * blockIdx.x / gridDim.x);
   const uint32_t u_end = static_cast<uint32_t>(static_cast<uint64_t>(total) * (blockIdx.x + 1) / gridDim.x);
@@ -230,48 +171,6 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Partial (this lane's) dot of one row with token j's activations.
-template <int F, int B, int CPL, int NT>
-__device__ __forceinline__ float row_dot_one(const RowRegs<F, B, CPL>& r, const XRegs<F, B, CPL, NT>& xr, int j,
-                                             int lane, int nchunks) {
-  using C = Codec<F, B>;
-  float acc = 0.0f;
-#pragma unroll
-  for (int m = 0; m < CPL; ++m) {
-    const bool ok = lane + 64 * m < nchunks;
-    uint32_t p[16];
-    C::pairs(r.w[m], p);
-    float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      d0 = dot2_bf16(p[i], xr.px[j][m][i], d0);
-      d1 = dot2_bf16(p[i + 1], xr.px[j][m][i + 1], d1);
-    }
-    const float d = d0 + d1;
-    if constexpr (F == 0) {
-      const float s = ok ? f16_to_f32(static_cast<uint16_t>(r.s[m])) : 0.0f;
-      const float b = ok ? f16_to_f32(static_cast<uint16_t>(r.b[m])) : 0.0f;
-      acc += s * d + (b - C::kOff * s) * xr.xs[j][m];
-    } else {
-      acc += d * (ok ? e8m0_to_f32(r.s[m]) : 0.0f);
-    }
-  }
-  return acc;
-}
-
-// The k selected experts' down rows of one output row, as loaded by a wave.
-template <int F, int B, int K>
-struct RoutedRows {
-  RowRegs<F, B, 1> r[K];
-};
-
-template <int F, int B, int K>
-__device__ __forceinline__ void dec_load_routed(RoutedRows<F, B, K>& b, const QMat (&qd)[K], int r, int lane,
-                                                int nchunks) {
-#pragma unroll
-  for (int j = 0; j < K; ++j) load_row<F, B, 1>(b.r[j], qd[j], r, lane, nchunks);
-}
-
 // Output row r of token t: the lane's partial of the shared row (ysh) plus the
 // weighted partials of the k routed rows, reduced over the wave and stored.
 template <int F, int B, int K>
@@ -299,11 +198,12 @@ constexpr int kDecSegRows = 4;  // output rows per segment of a wave's range
 // segment's shared rows are loaded first (for the first segment, before the
 // routing ids are even read, so that stream hides the ids' round trip), then
 // its routed rows, one row ahead of the arithmetic.
-template <int F, int B, int K, bool SH>
+// FULL: both input widths (intermediate sizes) are exactly 64 chunks of 32.
+template <int F, int B, int K, bool SH, bool FULL>
 __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int rows = a.down.rows, I = a.down.cols, nchunks = I >> 5;
-  const int Ish = SH ? a.sdown.cols : 32, nchunks_sh = Ish >> 5;
+  const int rows = a.down.rows, I = FULL ? 2048 : a.down.cols, nchunks = I >> 5;
+  const int Ish = SH ? (FULL ? 2048 : a.sdown.cols) : 32, nchunks_sh = Ish >> 5;
   const int64_t total = static_cast<int64_t>(a.T) * rows;
   const int64_t W = static_cast<int64_t>(gridDim.x) * 4, gw = static_cast<int64_t>(blockIdx.x) * 4 + wave;
   int64_t u = total * gw / W;
@@ -477,11 +377,16 @@ hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
   const int cus = device_cus();
   if (a.T == 1 && cus > 0 && cpl <= 2) {  // (hidden > 4096 would spill at 512 threads)
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(cus, static_cast<int64_t>(a.k) * a.gate.rows))), block(512);
+    const bool full = a.gate.cols == 2048 * cpl;
     QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
-      if (cpl == 1)
-        QSMOE_LAUNCH((k_dec_gateup1<F, B, 1>), grid, block, 0, s, a);
+      if (cpl == 1 && full)
+        QSMOE_LAUNCH((k_dec_gateup1<F, B, 1, true>), grid, block, 0, s, a);
+      else if (cpl == 1)
+        QSMOE_LAUNCH((k_dec_gateup1<F, B, 1, false>), grid, block, 0, s, a);
+      else if (full)
+        QSMOE_LAUNCH((k_dec_gateup1<F, B, 2, true>), grid, block, 0, s, a);
       else
-        QSMOE_LAUNCH((k_dec_gateup1<F, B, 2>), grid, block, 0, s, a);
+        QSMOE_LAUNCH((k_dec_gateup1<F, B, 2, false>), grid, block, 0, s, a);
     })
     return hipGetLastError();
   }
@@ -501,12 +406,17 @@ hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.down.rows, kDecDnMinRows)), block(256);
   const size_t lds = 0;
   const int K = a.k <= 2 ? 2 : (a.k <= 4 ? 4 : (a.k <= 6 ? 6 : 8));
+  const bool full = a.down.cols == 2048 && (!a.has_shared || a.sdown.cols == 2048);
 #define QSMOE_K3(K_)                                                                                   \
   do {                                                                                                 \
-    if (a.has_shared)                                                                                  \
-      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, true>), grid, block, lds, s, a);                \
+    if (a.has_shared && full)                                                                          \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, true, true>), grid, block, lds, s, a);                \
+    else if (a.has_shared)                                                                             \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, true, false>), grid, block, lds, s, a);               \
+    else if (full)                                                                                     \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, false, true>), grid, block, lds, s, a);               \
     else                                                                                               \
-      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, false>), grid, block, lds, s, a);               \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, false, false>), grid, block, lds, s, a);              \
   } while (0)
   QSMOE_DEC_FMT(a.down.fmt, a.down.bits, {
     if (K == 2) QSMOE_K3(2);

@@ -10,13 +10,15 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
-constexpr int kProbeBlocks = 2048;  // workgroups of the stream kernels (8 per CU)
+constexpr int kProbeBlocks = 2048;  // workgroups of the stream kernels (8 per CU); words of the sink
 
 // Mode 0: every byte of [src, src + bytes) read once, 16 bytes per lane,
 // consecutive lanes on consecutive 16-byte pieces. Mode 1: the first 32 bytes
 // of every 128-byte line (two 16-byte loads per lane, lanes 128 bytes apart).
-// The XOR of the words read goes to sink[0] (one atomic per workgroup), so
-// no load can be dropped. bytes is a multiple of 128.
+// The XOR of the words a workgroup read goes to sink[workgroup] (a plain
+// store: atomics on one word from every workgroup would serialise and cost
+// more than a small read), so no load can be dropped. bytes is a multiple of
+// 128.
 template <int MODE>
 __global__ __launch_bounds__(256) void k_probe_read(const u32x4_t* __restrict__ src, size_t bytes,
                                                     uint32_t* __restrict__ sink) {
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void k_probe_read(const u32x4_t* __restrict__ 
   __shared__ uint32_t s_x[4];
   if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = v;
   __syncthreads();
-  if (threadIdx.x == 0) atomicXor(sink, s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3]);
+  if (threadIdx.x == 0) sink[blockIdx.x] = s_x[0] ^ s_x[1] ^ s_x[2] ^ s_x[3];
 }
 
 // Every 16-byte piece of [dst, dst + bytes) written once with its index.

@@ -171,6 +171,10 @@ def test_deterministic_with_poisoned_workspace():
      ["dec_router", "dec_gateup", "dec_down_combine"]),
     (variant("decode", "disp_dec1", 220, T=1, d=512, I=256, E=32, I_shared=256),
      ["dec_router", "dec_gateup", "dec_down_combine"]),
+    (variant("decode", "disp_dec1_k8", 225, T=1, d=512, I=256, E=32, top_k=8, I_shared=256),
+     ["dec_router", "dec_gateup", "dec_down_combine"]),
+    (variant("hash", "disp_hash_dec1", 226, T=1, d=512, I=256, E=64, vocab=1000),
+     ["dec_router", "dec_gateup", "dec_down_combine"]),
     (variant("mixed", "disp_mixed_gemv", 214, T=20, d=512, I=256, E=128, top_k=4, I_shared=256),
      ["router_logits", "router_topk", "permute", "shared_gateup_mfma", "routed_gateup", "shared_down_mfma",
       "routed_down", "combine"]),
@@ -196,8 +200,7 @@ def test_deterministic_with_poisoned_workspace():
 ], ids=lambda v: v.name if hasattr(v, "name") else "")
 def test_dispatch_picks_expected_kernels(cfg, expect):
     """Which kernels a step runs: the fused path for up to 4 tokens (top-k or
-    hash routing); the
-    streaming GEMV under one token per expert (2/3-bit) or four (4-bit); the
+    hash routing); the streaming GEMV under one token per expert (2/3-bit) or four (4-bit); the
     matrix-core grouped GEMM above that; the shared expert on the matrix cores
     from 8 tokens, its K split over workgroups (with finishers) while its
     tiles are few."""

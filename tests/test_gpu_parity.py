@@ -9,8 +9,8 @@ and weights included); permutations equal the stable sort of the GPU's ids
 exactly; routed, shared and combined outputs within max relative error 2e-3
 per token (fp32 output mode); the bf16 output is the round-to-nearest-even of
 the fp32 output, bit for bit; the one-shot forward (which for up to 4 tokens
-takes the fused path) agrees with the four entry points called in turn to 1e-5;
-its bf16 h equals the oracle's rounding of float64 h except for flips at
+takes the fused path) agrees with the four entry points called in turn within
+the same bound; its bf16 h equals the oracle's rounding of float64 h except for flips at
 rounding midpoints, and its down projection, shared expert and combine agree
 with float64 arithmetic on that h to 1e-5.
 """
@@ -123,8 +123,11 @@ def check_layer(cfg, layer, dl, step):
         assert e_sh.max() <= TOL, e_sh.max()
     e = rel_err(out_f32.cpu().numpy(), ref.y)
     assert e.max() <= TOL, e.max()
-    # one-shot forward (which may take the fused small-batch path) vs the four entry points
-    assert rel_err(out_f32.cpu().numpy(), st.out.cpu().numpy().astype(np.float64)).max() <= 1e-5
+    # one-shot forward vs the four entry points: the one-shot call may run other
+    # kernels (the fused small-batch path, gate/up on the matrix cores), whose
+    # bf16 h can differ from the streaming GEMV's by rounding flips; each is
+    # held to the oracle above and, on its own h, to 1e-5 below
+    assert rel_err(out_f32.cpu().numpy(), st.out.cpu().numpy().astype(np.float64)).max() <= TOL
     assert torch.equal(out_f32.to(torch.bfloat16), out_bf16)
     flips = check_forward_intermediates(cfg, layer, dl, ws, x, tok, out_f32.cpu().numpy())
     print(f"{cfg.name} step {step}: {flips} h rounding flip(s) of {cfg.T * cfg.top_k * cfg.I}")

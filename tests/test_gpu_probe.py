@@ -17,10 +17,10 @@ def test_stream_reads_cover_exactly_their_bytes():
     buf = torch.from_numpy(host.view(np.int32)).cuda()
     for mode, want in [(0, np.bitwise_xor.reduce(host)),
                        (1, np.bitwise_xor.reduce(host.reshape(-1, 32)[:, :8].ravel()))]:
-        sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+        sink = torch.full((2048,), -1, dtype=torch.int32, device="cuda")
         qm.probe_stream(buf, mode, sink)
         torch.cuda.synchronize()
-        assert np.uint32(sink.cpu().numpy().view(np.uint32)[0]) == want, mode
+        assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == want, mode
 
 
 def test_stream_write_covers_every_piece():

@@ -68,6 +68,7 @@ CASES = [
     (variant("decode", "q_fused4_t3", 175, T=3, d=512, I=256, E=32, top_k=4, I_shared=256), FUSED),
     (variant("decode", "q_fused4_t4", 176, T=4, d=512, I=256, E=32, top_k=4, I_shared=256), FUSED),
     (variant("mixed", "q_fused23_t1", 177, T=1, d=1024, I=256, E=64, top_k=6, I_shared=256), FUSED),
+    (variant("mixed", "q_fused23_t1_k8", 185, T=1, d=1024, I=256, E=64, top_k=8, I_shared=256), FUSED),
     (variant("mixed", "q_fused8_t2", 178, T=2, d=512, I=256, E=16, top_k=2, gate_up=AFF8_G64, down=AFF8_G32,
              I_shared=256), FUSED),
     (variant("prefill", "q_mfma4", 179, T=96, d=512, I=256, E=8, top_k=2, bias_kind="normal", gate_up=AFF4_G64,
