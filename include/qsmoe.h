@@ -196,7 +196,8 @@ size_t moe_workspace_size(const moe_layer* layer, int32_t max_tokens);
  *                           (row p belongs to assignment perm[p]) on the
  *                           general path, slot order t*k + j on the fused path
  *   h_shared bf16  [T][I_shared] (shared expert)
- *   y_slot   fp32  [T*k][d], y_shared fp32 [T][d]  (general path only)
+ *   y_slot   fp32  [T*k][d]  (general path only), y_shared fp32 [T][d] (general
+ *            path, and the fused path of a single token)
  * fused = 1 when moe_forward takes the three-launch small-batch path. total =
  * the bytes moe_forward needs for exactly T tokens. Errors: INVALID_ARG (T <
  * 1, null out, invalid layer), UNSUPPORTED.

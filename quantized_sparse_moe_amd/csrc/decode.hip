@@ -93,63 +93,74 @@ __global__ __launch_bounds__(256) void k_dec_gateup(DecodeArgs a) {
   __syncthreads();
 }
 
-// Launch 2 for a single token: one 512-thread workgroup per CU takes an equal
-// share of the (slot, row) units, and inside it the 8 waves take rows one at
-// a time from an LDS counter, the next row's loads issued before the current
-// row is computed. Two waves share each SIMD and the older one is issued
-// first: with a fixed split per wave (or per workgroup, two per CU) the
-// younger half measured ~20 % slower and the launch ended with it.
-// FULL: the input width is exactly 64 CPL chunks of 32 (every lane's
-// chunks exist): validity masks and address clamps fold away.
-template <int F, int B, int CPL, bool FULL>
-__global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
-  __shared__ int32_t s_ids[kDecMaxK];
-  __shared__ uint32_t s_next;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    int id;
-    float wt;
-    dec_token_head(a, 0, blockIdx.x == 0, id, wt);
-    if (lane < a.k) {
-      s_ids[lane] = id;
-      if (blockIdx.x == 0) {
-        a.ids[lane] = id;
-        a.w[lane] = wt;
-      }
-    }
+// The shared expert's down rows [*ctr, end) of the single token, taken one
+// at a time from an LDS counter (next row's loads issued before the current
+// row is computed): y_sh[r] = down row r . h_sh, fp32. Takes no further row
+// once *stop is non-zero (stop may be null). Requires end > 0.
+__device__ __forceinline__ void dec_shared_down_rows(const DecodeArgs& a, uint32_t* ctr, uint32_t end, int lane,
+                                                     const uint32_t* stop) {
+  const int nchunks = a.sdown.cols >> 5;
+  auto grab = [&]() -> uint32_t {
+    if (stop != nullptr && __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u) return end;
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(ctr, 1u);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  const uint16_t* srow[1] = {a.h_sh};
+  const bool sv[1] = {true};
+  XRaw<1, 1> hw;
+  load_x_raw<1, 1>(hw, srow, lane, nchunks);
+  RowRegs<0, 8, 1> A, Bb;
+  XRegs<0, 8, 1, 1> hs;
+  auto compute = [&](const RowRegs<0, 8, 1>& r, uint32_t u) {
+    const float v[1] = {row_dot_one<0, 8, 1, 1>(r, hs, 0, lane, nchunks)};
+    const float y = wave_reduce_multi<1>(v);
+    if (reduce_multi_writer<1>(lane)) a.y_sh[u] = y;
+  };
+  uint32_t u0 = grab();
+  load_row<0, 8, 1>(A, a.sdown, min(u0, end - 1), lane, nchunks);
+  finish_x<0, 8, 1, 1>(hs, hw, sv, lane, nchunks);
+  if (u0 >= end) return;
+  while (true) {
+    const uint32_t u1 = grab();
+    load_row<0, 8, 1>(Bb, a.sdown, min(u1, end - 1), lane, nchunks);
+    compute(A, u0);
+    if (u1 >= end) break;
+    const uint32_t u2 = grab();
+    load_row<0, 8, 1>(A, a.sdown, min(u2, end - 1), lane, nchunks);
+    compute(Bb, u1);
+    if (u2 >= end) break;
+    u0 = u2;
   }
+}
+
+// The routed (slot, row) units [*ctr, u_end) of k_dec_gateup1 (u_end > 0).
+template <int F, int B, int CPL, bool FULL>
+__device__ __forceinline__ void dec_gateup1_rows(const DecodeArgs& a, const int32_t* s_ids, uint32_t* ctr,
+                                                 uint32_t u_end, const XRaw<CPL, 1>& xw, int lane) {
   const int rows = a.gate.rows, nchunks = FULL ? 64 * CPL : a.gate.cols >> 5;
-  const uint32_t total = static_cast<uint32_t>(a.k) * rows;
-  const uint32_t u_begin = static_cast<uint32_t>(static_cast<uint64_t>(total) * blockIdx.x / gridDim.x);
-  const uint32_t u_end = static_cast<uint32_t>(static_cast<uint64_t>(total) * (blockIdx.x + 1) / gridDim.x);
-  if (threadIdx.x == 0) s_next = u_begin;
-  const uint16_t* xrow[1] = {a.x};
   const bool xvalid[1] = {true};
-  XRaw<CPL, 1> xw;
-  load_x_raw<CPL, 1>(xw, xrow, lane, nchunks);
-  __syncthreads();
-  if (u_begin >= u_end) return;
   auto grab = [&]() -> uint32_t {
     uint32_t v = 0;
-    if (lane == 0) v = atomicAdd(&s_next, 1u);
+    if (lane == 0) v = atomicAdd(ctr, 1u);
     return __builtin_amdgcn_readfirstlane(v);
   };
   using Batch = RowBatch<F, B, CPL, true, 1>;
   // loads are unconditional: a unit past the end reloads the last one
-  auto load_unit = [&](Batch& b, uint32_t u) {
+  auto load_unit = [&](Batch& bt, uint32_t u) {
     const uint32_t uc = min(u, u_end - 1);
     const int slot = static_cast<int>(uc / rows), r = static_cast<int>(uc - static_cast<uint32_t>(slot) * rows);
     const int e = min(max(__builtin_amdgcn_readfirstlane(s_ids[slot]), 0), a.E - 1);
-    load_batch<F, B, CPL, true, 1>(b, expert_slice(a.gate, e), expert_slice(a.up, e), r, r + 1, lane, nchunks);
+    load_batch<F, B, CPL, true, 1>(bt, expert_slice(a.gate, e), expert_slice(a.up, e), r, r + 1, lane, nchunks);
   };
   XRegs<F, B, CPL, 1> xr;
-  auto compute_unit = [&](const Batch& b, uint32_t u) {
+  auto compute_unit = [&](const Batch& bt, uint32_t u) {
     const int slot = static_cast<int>(u / rows), r = static_cast<int>(u - static_cast<uint32_t>(slot) * rows);
     uint16_t* hs = a.h + static_cast<size_t>(slot) * rows;
     auto store = [&](int, int rr, float g, float up) {
       hs[rr] = static_cast<uint16_t>(f32_to_bf16_rne(silu(g) * up));
     };
-    compute_batch<F, B, CPL, 1, true, 1>(b, xr, r, r + 1, lane, nchunks, store);
+    compute_batch<F, B, CPL, 1, true, 1>(bt, xr, r, r + 1, lane, nchunks, store);
   };
   Batch A, Bb;
   uint32_t u0 = grab();
@@ -170,17 +181,80 @@ __global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
   }
 }
 
+// Launch 2 for a single token: one 512-thread workgroup per CU takes an equal
+// share of the (slot, row) units, and inside it the 8 waves take rows one at
+// a time from an LDS counter, the next row's loads issued before the current
+// row is computed. Two waves share each SIMD and the older one is issued
+// first: with a fixed split per wave (or per workgroup, two per CU) the
+// younger half measured ~20 % slower and the launch ended with it.
+// While wave 0 selects the top-k, the other waves stream the shared
+// expert's down rows of the workgroup's share of the output rows (SHD: the
+// layer has a shared expert; it needs no routing, and launch 3 then only adds
+// y_sh); every wave joins the routed rows once the ids are in LDS, and the
+// shared rows left over are taken by the waves that run out of routed rows.
+// FULL: the input width is exactly 64 CPL chunks of 32 (every lane's
+// chunks exist): validity masks and address clamps fold away.
+template <int F, int B, int CPL, bool FULL, bool SHD>
+__global__ __launch_bounds__(512) void k_dec_gateup1(DecodeArgs a) {
+  __shared__ int32_t s_ids[kDecMaxK];
+  __shared__ uint32_t s_next, s_sh_next, s_ready;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int rows = a.gate.rows, nchunks = FULL ? 64 * CPL : a.gate.cols >> 5;
+  const uint32_t G = gridDim.x, b = blockIdx.x;
+  const uint32_t total = static_cast<uint32_t>(a.k) * rows;
+  const uint32_t u_begin = static_cast<uint32_t>(static_cast<uint64_t>(total) * b / G);
+  const uint32_t u_end = static_cast<uint32_t>(static_cast<uint64_t>(total) * (b + 1) / G);
+  const uint32_t d_rows = SHD ? static_cast<uint32_t>(a.sdown.rows) : 0u;
+  const uint32_t r0 = static_cast<uint32_t>(static_cast<uint64_t>(d_rows) * b / G);
+  const uint32_t r1 = static_cast<uint32_t>(static_cast<uint64_t>(d_rows) * (b + 1) / G);
+  if (threadIdx.x == 0) {
+    s_next = u_begin;
+    s_sh_next = r0;
+    s_ready = 0;
+  }
+  const uint16_t* xrow[1] = {a.x};
+  const bool xvalid[1] = {true};
+  XRaw<CPL, 1> xw;
+  load_x_raw<CPL, 1>(xw, xrow, lane, nchunks);
+  __syncthreads();
+  if (wave == 0) {
+    int id;
+    float wt;
+    dec_token_head(a, 0, b == 0, id, wt);
+    if (lane < a.k) {
+      s_ids[lane] = id;
+      if (b == 0) {
+        a.ids[lane] = id;
+        a.w[lane] = wt;
+      }
+    }
+    __hip_atomic_store(&s_ready, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else if constexpr (SHD) {
+    if (r0 < r1) dec_shared_down_rows(a, &s_sh_next, r1, lane, &s_ready);
+  }
+  // the ids (wave 0 always stores them; the poll is bounded all the same)
+  for (uint32_t it = 0; it < kLdsSpinLimit; ++it) {
+    if (__hip_atomic_load(&s_ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) != 0u) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (u_begin < u_end) dec_gateup1_rows<F, B, CPL, FULL>(a, s_ids, &s_next, u_end, xw, lane);
+  if constexpr (SHD) {
+    if (r0 < r1) dec_shared_down_rows(a, &s_sh_next, r1, lane, nullptr);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Output row r of token t: the lane's partial of the shared row (ysh) plus the
-// weighted partials of the k routed rows, reduced over the wave and stored.
+// weighted partials of the k routed rows, reduced over the wave, plus the
+// shared expert's output when launch 2 computed it (ypre), and stored.
 template <int F, int B, int K>
 __device__ __forceinline__ void dec_finish_row(const RoutedRows<F, B, K>& b, const XRegs<F, B, 1, K>& hx,
-                                               const float (&wj)[K], float ysh, const DecodeArgs& a, int t, int r,
-                                               bool valid, int lane, int nchunks) {
+                                               const float (&wj)[K], float ysh, float ypre, const DecodeArgs& a, int t,
+                                               int r, bool valid, int lane, int nchunks) {
   float v[1] = {ysh};
 #pragma unroll
   for (int j = 0; j < K; ++j) v[0] += wj[j] * row_dot_one<F, B, 1, K>(b.r[j], hx, j, lane, nchunks);
-  const float y = wave_reduce_multi<1>(v);
+  const float y = wave_reduce_multi<1>(v) + ypre;
   if (reduce_multi_writer<1>(lane) && valid) {
     const size_t o = static_cast<size_t>(t) * a.down.rows + r;
     if (a.out_f32)
@@ -194,13 +268,15 @@ constexpr int kDecSegRows = 4;  // output rows per segment of a wave's range
 
 // Launch 3: per (token, output row) unit, the k selected experts' down rows
 // and the shared expert's down row against their own h vectors, weighted and
-// summed in one reduction. A wave's rows go in segments of kDecSegRows: the
+// summed in one reduction (SHM 1; SHM 2: launch 2 computed the shared
+// expert's output y_sh, which is added; SHM 0: no shared expert). A wave's rows go in segments of kDecSegRows: the
 // segment's shared rows are loaded first (for the first segment, before the
 // routing ids are even read, so that stream hides the ids' round trip), then
 // its routed rows, one row ahead of the arithmetic.
 // FULL: both input widths (intermediate sizes) are exactly 64 chunks of 32.
-template <int F, int B, int K, bool SH, bool FULL>
+template <int F, int B, int K, int SHM, bool FULL>
 __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
+  constexpr bool SH = SHM == 1, PRE = SHM == 2;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int rows = a.down.rows, I = FULL ? 2048 : a.down.cols, nchunks = I >> 5;
   const int Ish = SH ? (FULL ? 2048 : a.sdown.cols) : 32, nchunks_sh = Ish >> 5;
@@ -255,6 +331,10 @@ __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
       }
       RoutedRows<F, B, K> A, Bb;
       dec_load_routed<F, B, K>(A, qd, min(seg0, r_end - 1), lane, nchunks);
+      float ypre[kDecSegRows];
+#pragma unroll
+      for (int i = 0; i < kDecSegRows; ++i)
+        ypre[i] = PRE ? a.y_sh[static_cast<size_t>(t) * rows + min(seg0 + i, r_end - 1)] : 0.0f;
       if constexpr (FIRST) {
         finish_x<F, B, 1, K>(hx, hw, hvalid, lane, nchunks);
       }
@@ -263,12 +343,12 @@ __global__ __launch_bounds__(256) void k_dec_down_combine(DecodeArgs a) {
       for (int i = 0; i < kDecSegRows; ++i)
         ysh[i] = SH ? row_dot_one<0, 8, 1, 1>(rs[i], hsx, 0, lane, nchunks_sh) : 0.0f;
       dec_load_routed<F, B, K>(Bb, qd, min(seg0 + 1, r_end - 1), lane, nchunks);
-      dec_finish_row<F, B, K>(A, hx, wj, ysh[0], a, t, seg0, seg0 < r_end, lane, nchunks);
+      dec_finish_row<F, B, K>(A, hx, wj, ysh[0], ypre[0], a, t, seg0, seg0 < r_end, lane, nchunks);
       dec_load_routed<F, B, K>(A, qd, min(seg0 + 2, r_end - 1), lane, nchunks);
-      dec_finish_row<F, B, K>(Bb, hx, wj, ysh[1], a, t, seg0 + 1, seg0 + 1 < r_end, lane, nchunks);
+      dec_finish_row<F, B, K>(Bb, hx, wj, ysh[1], ypre[1], a, t, seg0 + 1, seg0 + 1 < r_end, lane, nchunks);
       dec_load_routed<F, B, K>(Bb, qd, min(seg0 + 3, r_end - 1), lane, nchunks);
-      dec_finish_row<F, B, K>(A, hx, wj, ysh[2], a, t, seg0 + 2, seg0 + 2 < r_end, lane, nchunks);
-      dec_finish_row<F, B, K>(Bb, hx, wj, ysh[3], a, t, seg0 + 3, seg0 + 3 < r_end, lane, nchunks);
+      dec_finish_row<F, B, K>(A, hx, wj, ysh[2], ypre[2], a, t, seg0 + 2, seg0 + 2 < r_end, lane, nchunks);
+      dec_finish_row<F, B, K>(Bb, hx, wj, ysh[3], ypre[3], a, t, seg0 + 3, seg0 + 3 < r_end, lane, nchunks);
     };
     static_assert(kDecSegRows == 4, "the segment body is unrolled for 4 rows");
     segment(r_begin, std::true_type{});
@@ -372,22 +452,37 @@ static int device_cus() {
   return n;
 }
 
+// Launch 2 of a single token runs one 512-thread workgroup per CU
+// (k_dec_gateup1; a hidden size above 4096 would spill at 512 threads).
+static bool dec_single_token(const DecodeArgs& a) {
+  return a.T == 1 && dec_cpl(a.gate.cols) <= 2 && device_cus() > 0;
+}
+
+bool dec_shared_in_gateup(const DecodeArgs& a) { return a.has_shared && dec_single_token(a); }
+
 hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s) {
   const int cpl = dec_cpl(a.gate.cols);
-  const int cus = device_cus();
-  if (a.T == 1 && cus > 0 && cpl <= 2) {  // (hidden > 4096 would spill at 512 threads)
-    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(cus, static_cast<int64_t>(a.k) * a.gate.rows))), block(512);
+  if (dec_single_token(a)) {
+    const dim3 grid(static_cast<unsigned>(device_cus())), block(512);
     const bool full = a.gate.cols == 2048 * cpl;
+#define QSMOE_K2(CP, FU)                                                                   \
+  do {                                                                                     \
+    if (a.has_shared)                                                                      \
+      QSMOE_LAUNCH((k_dec_gateup1<F, B, CP, FU, true>), grid, block, 0, s, a);             \
+    else                                                                                   \
+      QSMOE_LAUNCH((k_dec_gateup1<F, B, CP, FU, false>), grid, block, 0, s, a);            \
+  } while (0)
     QSMOE_DEC_FMT(a.gate.fmt, a.gate.bits, {
       if (cpl == 1 && full)
-        QSMOE_LAUNCH((k_dec_gateup1<F, B, 1, true>), grid, block, 0, s, a);
+        QSMOE_K2(1, true);
       else if (cpl == 1)
-        QSMOE_LAUNCH((k_dec_gateup1<F, B, 1, false>), grid, block, 0, s, a);
+        QSMOE_K2(1, false);
       else if (full)
-        QSMOE_LAUNCH((k_dec_gateup1<F, B, 2, true>), grid, block, 0, s, a);
+        QSMOE_K2(2, true);
       else
-        QSMOE_LAUNCH((k_dec_gateup1<F, B, 2, false>), grid, block, 0, s, a);
+        QSMOE_K2(2, false);
     })
+#undef QSMOE_K2
     return hipGetLastError();
   }
   const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.k * a.gate.rows, kDecGuMinRows)), block(256);
@@ -406,17 +501,23 @@ hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(dec_grid(static_cast<int64_t>(a.T) * a.down.rows, kDecDnMinRows)), block(256);
   const size_t lds = 0;
   const int K = a.k <= 2 ? 2 : (a.k <= 4 ? 4 : (a.k <= 6 ? 6 : 8));
-  const bool full = a.down.cols == 2048 && (!a.has_shared || a.sdown.cols == 2048);
-#define QSMOE_K3(K_)                                                                                   \
+  const int shm = !a.has_shared ? 0 : (dec_shared_in_gateup(a) ? 2 : 1);
+  const bool full = a.down.cols == 2048 && (shm != 1 || a.sdown.cols == 2048);
+#define QSMOE_K3S(K_, SHM_)                                                                            \
   do {                                                                                                 \
-    if (a.has_shared && full)                                                                          \
-      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, true, true>), grid, block, lds, s, a);                \
-    else if (a.has_shared)                                                                             \
-      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, true, false>), grid, block, lds, s, a);               \
-    else if (full)                                                                                     \
-      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, false, true>), grid, block, lds, s, a);               \
+    if (full)                                                                                          \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, SHM_, true>), grid, block, lds, s, a);                \
     else                                                                                               \
-      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, false, false>), grid, block, lds, s, a);              \
+      QSMOE_LAUNCH((k_dec_down_combine<F, B, K_, SHM_, false>), grid, block, lds, s, a);               \
+  } while (0)
+#define QSMOE_K3(K_)            \
+  do {                          \
+    if (shm == 2)               \
+      QSMOE_K3S(K_, 2);         \
+    else if (shm == 1)          \
+      QSMOE_K3S(K_, 1);         \
+    else                        \
+      QSMOE_K3S(K_, 0);         \
   } while (0)
   QSMOE_DEC_FMT(a.down.fmt, a.down.bits, {
     if (K == 2) QSMOE_K3(2);
@@ -425,6 +526,7 @@ hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s) {
     else QSMOE_K3(8);
   })
 #undef QSMOE_K3
+#undef QSMOE_K3S
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@ namespace qsmoe {
 
 constexpr int kDecMaxT = 4;
 constexpr int kDecMaxK = 8;
+constexpr uint32_t kLdsSpinLimit = 1u << 24;  // polls of a workgroup-local flag before giving up
 // Hash route of token t by one wave (the pages' tid2eid table, as k_hash):
 // lane j < k takes expert tid2eid[token][j]; the weights are the launch-1
 // scores of those experts renormalised over the k slots (summed in slot

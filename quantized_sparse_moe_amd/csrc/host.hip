@@ -398,7 +398,8 @@ moe_status moe_workspace_layout(const moe_layer* layer, int32_t T, moe_ws_layout
   out->h = f.h;
   out->h_shared = L.shared ? f.h_sh : 0;
   out->y_slot = fused ? 0 : f.y_slot;
-  out->y_shared = L.shared && !fused ? f.y_sh : 0;
+  const bool y_sh = L.shared && (!fused || dec_shared_in_gateup(da));
+  out->y_shared = y_sh ? f.y_sh : 0;
   return MOE_OK;
 }
 
@@ -542,6 +543,7 @@ moe_status run_forward(const moe_layer& L, const uint16_t* x_bf16, const int32_t
       da.sup = to_qmat(L.shared->up);
       da.sdown = to_qmat(L.shared->down);
       da.h_sh = at<uint16_t>(ws, f.h_sh);
+      da.y_sh = at<float>(ws, f.y_sh);
     }
     da.out = out;
     da.out_f32 = out_dtype == MOE_OUT_F32;

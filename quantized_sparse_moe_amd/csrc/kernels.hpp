@@ -117,11 +117,14 @@ struct DecodeArgs {
   const int32_t* tid2eid;    // [vocab][k] (hash)
   int32_t vocab;
   int32_t* err;            // workspace error word
+  float* y_sh;             // workspace fp32 [T][d]: the shared expert's output (single token)
 };
 bool decode_path_supported(const DecodeArgs& a);
 hipError_t launch_dec_router(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dec_gateup(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dec_down_combine(const DecodeArgs& a, hipStream_t s);
+// Launch 2 computes the shared expert's down projection into y_sh (single token).
+bool dec_shared_in_gateup(const DecodeArgs& a);
 
 // Combine --------------------------------------------------------------------
 hipError_t launch_combine(const float* y_slot, const float* w, const float* y_shared, int T, int k, int d,

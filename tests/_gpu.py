@@ -247,8 +247,8 @@ def check_forward_intermediates(cfg, layer, dl, ws, x, tok, out_f32):
         y_sh = oracle.bf16_bits_to_f64(r["h_shared"]) @ ref["w2"].T
     if not r["fused"]:
         assert rel_err(r["y_slot"], y_tight).max() <= TIGHT
-        if layer.shared is not None:
-            assert rel_err(r["y_shared"], y_sh).max() <= TIGHT
+    if r["y_shared"] is not None:
+        assert rel_err(r["y_shared"], y_sh).max() <= TIGHT
     y = np.einsum("tk,tkd->td", w.astype(np.float64), y_tight.reshape(T, k, cfg.d)) + y_sh
     assert rel_err(out_f32, y).max() <= TIGHT
     return flips
