@@ -72,14 +72,16 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds) {
 // s_waitcnt vmcnt(0), leaving the LDS/scalar and export counters alone
 // (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 __device__ __forceinline__ void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
-// Workgroup barrier that leaves the wave's 4 newest vector loads in flight:
-// s_waitcnt vmcnt(4) lgkmcnt(0), then s_barrier between compiler-only fences
-// (they keep LDS accesses from moving across; a release fence would make the
-// wave wait for every load in flight, since the compiler cannot tell
-// direct-to-LDS loads from register loads). Loads complete in order, so
-// everything older than the 4 newest has landed.
-__device__ __forceinline__ void barrier_keep4() {
-  __builtin_amdgcn_s_waitcnt(0x0074);
+// Workgroup barrier that leaves the wave's N newest vector loads in flight
+// (N < 16): s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier between
+// compiler-only fences (they keep LDS accesses from moving across; a release
+// fence would make the wave wait for every load in flight, since the compiler
+// cannot tell direct-to-LDS loads from register loads). Loads complete in
+// order, so everything older than the N newest has landed.
+template <int N>
+__device__ __forceinline__ void barrier_keep() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -327,251 +329,220 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4(MfmaArgs a) {
   }
 }
 
-// waves per workgroup in k_mfma_mxfp4_w (4: two workgroups per CU; 8 waves
-// over 512 columns, one workgroup per CU, measured slower: 1000 -> 1025 us)
-constexpr int kMxwWaves = 4;
-// most K steps per scale load in k_mfma_mxfp4_w (1, 2 or 4)
-constexpr int kMxfp4ScaleSteps = 4;
-
 // ---------------------------------------------------------------------------
-// MXFP4 grouped GEMM on 32 x 32 tiles (V_MFMA_F32_32X32X16_BF16).
+// MXFP4 grouped GEMM on 32 x 32 tiles (V_MFMA_F32_32X32X16_BF16), weights
+// staged through LDS, two workgroups per CU.
 //
 // Workgroup: 128 bucketed tokens x 256 output columns: 128 rows of gate and
 // the same 128 rows of up, or 256 rows of down. Its 4 waves split the
 // columns; each takes all 128 tokens x 64 columns (gate/up: 32 rows of gate
 // + the same 32 of up, so the SwiGLU pairs meet in one lane) as 4 x 2
-// accumulator tiles of 32 x 32. (A 2 x 2 grid of waves, each 64 tokens x
-// 64 columns, loads and converts every weight twice and measured slower.)
-// Operand layouts (checked on the device): A lane l holds row
-// l % 32, inputs 8 (l / 32) .. + 7 of the pass; B lane l holds column l % 32
-// and the same inputs; element i of D in lane l is row
+// accumulator tiles of 32 x 32. Operand layouts (checked on the device): A
+// lane l holds row l % 32, inputs 8 (l / 32) .. + 7 of the pass; B lane l
+// holds column l % 32 and the same inputs; element i of D in lane l is row
 // 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32. In a 128-input K step lane
 // group g = l / 32 holds inputs 64 g .. 64 g + 63, pass p (0..7) using inputs
 // 64 g + 8 p .. + 7 for A and B alike (the sum does not care which pass adds
-// which input), so a lane's weights for the whole step are 32 contiguous
-// bytes of its row (two 16-byte loads) with the two e8m0 exponents that
-// cover them. Per pass a wave reads 4 activation fragments from LDS and
-// converts 2 weight fragments for 8 MFMAs of 32 x 32 x 16.
-template <bool GATEUP, int SCS>
-__global__ __launch_bounds__(64 * kMxwWaves, 8 / kMxwWaves) void k_mfma_mxfp4_w(MfmaArgs a) {
+// which input), so a lane's weights for the step are 32 contiguous bytes of
+// its row with the two e8m0 exponents over them.
+//
+// Loads. Every operand goes from HBM straight into LDS
+// (GLOBAL_LOAD_LDS_DWORDX4, 16 bytes per lane, no staging registers):
+//  - activations (gathered through perm for gate/up; contiguous bucketed h
+//    rows for down), double-buffered one K step ahead: a load instruction
+//    covers 4 tile rows x 256 bytes; rows of 256 bytes, slot s of row r
+//    holding input chunk s ^ (r % 16), so the 16 rows that 16 lanes read at
+//    once hold a chunk in 16 different slots;
+//  - weights: each wave loads its own 64 rows x 64 bytes of the step, 16 rows
+//    x 64 contiguous bytes per instruction (a load straight into the B operand
+//    layout touches 32 rows per instruction, and a 64-lane load costs about
+//    in proportion to the 128-byte lines it touches: measured on this GPU,
+//    34 against 20 bytes per clock per CU from L2). A row's four 16-byte
+//    chunks sit at slot c ^ ((r / 4) % 4) of its 64 bytes, so the 16 rows that
+//    16 lanes read at once cover all 64 banks. The rows are private to the
+//    wave, so a single buffer suffices: the wave copies the step's 32 bytes
+//    per lane and block into registers, then issues the next step's loads
+//    into the same place;
+//  - the e8m0 bytes of 4 K steps in one 16-byte load per block, 4 steps ahead.
+// The LDS budget (2 x 32 KB activations + 16 KB weights, the set-up's
+// offsets aliased into the weight buffer) leaves room for two workgroups per
+// CU, which hide each other's barriers, set-up and epilogue. The weights
+// become exact bf16 with v_cvt_scalef32_pk_bf16_fp4 (the scale applied in the
+// conversion).
+template <bool GATEUP>
+__global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
   typedef __attribute__((ext_vector_type(16))) float f32x16_t;
-  constexpr int NW = kMxwWaves;
   constexpr int MT = 128;
-  constexpr int MTW = MT / 32;                   // 32-token tiles per wave
-  constexpr int NTILE = (GATEUP ? 32 : 64) * NW;  // output rows per workgroup (per matrix)
-  constexpr int ACH = MT * 16 / (64 * NW);       // 16-byte activation chunks per thread per K step
-  extern __shared__ int32_t s_dyn[];        // expert offsets and m-tile starts, E + 1 each
-  int32_t* const s_off = s_dyn;
-  int32_t* const s_mt = s_dyn + a.E + 1;
-  __shared__ int32_t s_src[MT];
-  // the two activation buffers are separate objects, so the compiler can
-  // tell reads of one from the direct-to-LDS loads into the other
-  __shared__ __attribute__((aligned(16))) uint16_t s_a0[MT * kKT];
-  __shared__ __attribute__((aligned(16))) uint16_t s_a1[MT * kKT];
+  constexpr int NB = 2;                              // 32-column blocks per wave
+  constexpr int WR = 32 * NB;                        // weight rows per wave
+  constexpr int NTILE = GATEUP ? 2 * WR : 4 * WR;    // rows per matrix per workgroup
+  constexpr int ACH = MT * 16 / 256;                 // 16-byte activation chunks per thread per step
+  constexpr int WCH = WR * 4 / 64;                   // weight load instructions per wave per step
+  constexpr int ABUF = MT * kKT * 2;                 // bytes per activation buffer
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
+  uint16_t* const s_a0 = reinterpret_cast<uint16_t*>(s_lds);
+  uint16_t* const s_a1 = reinterpret_cast<uint16_t*>(s_lds + ABUF);
+  uint8_t* const s_w = s_lds + 2 * ABUF;             // 4 waves x WR rows x 64 bytes
+  // the set-up's expert offsets, m-tile starts and gather rows live in the
+  // weight buffer until its first load
+  int32_t* const s_off = reinterpret_cast<int32_t*>(s_w);
+  int32_t* const s_mt = s_off + a.E + 1;
+  int32_t* const s_src = s_off;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, r32 = lane & 31;
-  const int wn = wave;
   const int n = a.T * a.k;
   const int rows = a.m0.rows, cols = a.m0.cols;
   Tile t;
   if (!tile_of_block<MT>(a, rows / NTILE, s_off, s_mt, t)) return;
   const int e = __builtin_amdgcn_readfirstlane(t.e), p0 = __builtin_amdgcn_readfirstlane(t.p0);
   const int count = __builtin_amdgcn_readfirstlane(t.count), ntile = __builtin_amdgcn_readfirstlane(t.ntile);
+  __syncthreads();  // every wave is done with s_off / s_mt
   if (tid < MT) {
     const int p = p0 + min(tid, count - 1);
     s_src[tid] = GATEUP && !a.shared ? min(max(a.perm[p] / a.k, 0), a.T - 1) : p;
   }
   __syncthreads();
-
-  // activations: direct global -> LDS loads, 16 bytes per lane. Round i of
-  // wave w fills the 1 KB of tile rows 4 b .. 4 b + 3, b = ACH w + i: lane l
-  // writes slot l % 16 of row 4 b + l / 16 (rows of 256 bytes, unpadded), and
-  // slot s of row r holds input chunk s ^ (r % 16) of the step, so the 16
-  // rows that 16 lanes read at once hold a chunk in 16 different slots (no
-  // bank conflicts). Rows past the tile's tokens repeat its last token.
+  // activations: round i of wave w fills the 1 KB of tile rows 4 b .. 4 b + 3,
+  // b = ACH w + i (wave w: rows 32 w .. 32 w + 31). Rows past the tile's
+  // tokens repeat its last token.
   uint32_t a_off[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
     const int row = 4 * (ACH * wave + i) + (lane >> 4), slot = lane & 15;
     a_off[i] = static_cast<uint32_t>(s_src[row]) * cols + 8 * (slot ^ (row & 15));
   }
-  auto load_a = [&](uint16_t* buf, int k0) {
+  __syncthreads();  // s_src is read: the weight buffer is free
+  auto load_a = [&](uint16_t* buf, int k) {
+    const uint16_t* const base = a.x + k * kKT;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      load_lds16(a.x + a_off[i] + k0, buf + (ACH * wave + i) * 512);
+    for (int i = 0; i < ACH; ++i) load_lds16(base + a_off[i], buf + (ACH * wave + i) * 512);
   };
   // fragment reads: lane (r32, g) takes chunk 8 g + p of its row in pass p
   const int xr = r32 & 15;
   const int a_rd = r32 * kKT + 8 * ((8 * g) ^ (xr & 8));
 
-  // weights: block 0 = rows row0 of gate (or down), block 1 = the same rows
-  // of up (or rows row0 + 32 of down)
+  // weights: block b of the wave is rows wrow(b) .. + 31 of gate (b = 0) and
+  // up (b = 1), or of down
   const QMat w0 = expert_slice(a.m0, e);
   const QMat w1 = expert_slice(a.m1, e);
-  const int row0 = ntile * NTILE + wn * (GATEUP ? 32 : 64) + r32;
   const size_t rb_bytes = static_cast<size_t>(w0.row_words) * 4, rg = static_cast<size_t>(w0.row_groups);
-  const uint8_t* cb[2];
-  const uint8_t* sb[2];  // the row's e8m0 bytes
-  cb[0] = reinterpret_cast<const uint8_t*>(w0.codes) + static_cast<size_t>(row0) * rb_bytes + 32 * g;
-  sb[0] = static_cast<const uint8_t*>(w0.scales) + static_cast<size_t>(row0) * rg;
-  if constexpr (GATEUP) {
-    cb[1] = reinterpret_cast<const uint8_t*>(w1.codes) + static_cast<size_t>(row0) * rb_bytes + 32 * g;
-    sb[1] = static_cast<const uint8_t*>(w1.scales) + static_cast<size_t>(row0) * rg;
-  } else {
-    cb[1] = cb[0] + 32 * rb_bytes;
-    sb[1] = sb[0] + 32 * rg;
+  auto wrow = [&](int b) { return GATEUP ? ntile * NTILE + 32 * wave : ntile * NTILE + WR * wave + 32 * b; };
+  const uint8_t* wbase[NB];
+  const uint8_t* sbase[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const QMat& m = (GATEUP && b == 1) ? w1 : w0;
+    wbase[b] = reinterpret_cast<const uint8_t*>(m.codes) + static_cast<size_t>(wrow(b)) * rb_bytes;
+    sbase[b] = static_cast<const uint8_t*>(m.scales) + static_cast<size_t>(wrow(b) + r32) * rg;
   }
-  struct BRegs {
-    u32x4_t c[2][2];  // [block][half]: 32 bytes = 64 codes
-    uint32_t s[2];    // [block]: the two e8m0 bytes of the step (groups 2g, 2g + 1), SCS == 1
-  };
-  auto load_b = [&](BRegs& b, int k0) {
+  // weight load instruction i covers the wave's rows 16 i .. 16 i + 15
+  // (block i / 2): lane l takes row 16 i + l / 4, LDS slot l % 4, global
+  // chunk (l % 4) ^ ((row / 4) % 4)
+  uint32_t w_off[WCH];
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const uint8_t* cp = cb[blk] + k0 / 2;
-      b.c[blk][0] = *reinterpret_cast<const u32x4_t*>(cp);
-      b.c[blk][1] = *reinterpret_cast<const u32x4_t*>(cp + 16);
-      if constexpr (SCS == 1) b.s[blk] = *reinterpret_cast<const uint16_t*>(sb[blk] + k0 / 32 + 2 * g);
-    }
+  for (int i = 0; i < WCH; ++i) {
+    const int rl = 16 * i + (lane >> 2);
+    const int c = (lane & 3) ^ ((rl >> 2) & 3);
+    w_off[i] = static_cast<uint32_t>((rl & 31) * rb_bytes + 16 * c);
+  }
+  uint8_t* const w_lds = s_w + WR * wave * 64;
+  auto load_w = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < WCH; ++i) load_lds16(wbase[i / 2] + k * (kKT / 2) + w_off[i], w_lds + 16 * i * 64);
   };
+  // block b, half h (passes 4 h .. 4 h + 3) is chunk 2 g + h of row 32 b + r32
+  uint32_t w_rd[NB][2];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int rl = 32 * b + r32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) w_rd[b][h] = rl * 64 + 16 * ((2 * g + h) ^ ((rl >> 2) & 3));
+  }
 
-  const int nmt = min(MTW, (count + 31) / 32);  // 32-token tiles with tokens
-  const int nsteps = cols / kKT;
-  // Activations one K step ahead in LDS; weights D - 1 steps ahead in a
-  // register ring of D. D = 4 where the accumulators leave the registers
-  // (under 4 token blocks with tokens) and the scales come in 4-step chunks;
-  // since loads complete in order and every step waits for its activation
-  // loads, a weight load then has two steps to land instead of one.
-  auto kloop = [&](auto nmt_tag, auto d_tag) {
+  const int nmt = min(MT / 32, (count + 31) / 32);  // 32-token blocks with tokens
+  const int nsteps = cols / kKT;                     // a multiple of 4
+  // a wave whose activation rows all lie in blocks without tokens loads none
+  const bool a_need = wave < nmt;
+
+  // K loop specialised on the number of token blocks with tokens: the
+  // accumulators and MFMAs of empty blocks do not exist
+  auto kloop = [&](auto nmt_tag) {
     constexpr int NMT = decltype(nmt_tag)::value;
-    constexpr int D = decltype(d_tag)::value;
-    static_assert(D == 2 || (D == 4 && SCS == 4), "a 4-deep ring takes 4-step scale chunks");
-    // CS > 1: the e8m0 bytes of CS K steps in one 4 CS-byte load per block
-    // (byte 4 j + 2 g + h = group 2 g + h of step j), issued one step (D = 2)
-    // or four steps (D = 4) before the first of them is needed. A 2-byte load
-    // per lane and step costs about as much as a 16-byte one: each touches
-    // 32 rows' cache lines. (With all 4 token blocks, 4-step chunks and a
-    // 2-deep ring exceed the registers.)
-    constexpr int CS = D == 4 ? 4 : (SCS < 2 ? SCS : 2);
-    typedef __attribute__((ext_vector_type(CS))) uint32_t scv_t;
-    scv_t scn[2], s_nxt[2];  // the current chunk; D == 4: the next one
-    auto load_sn = [&](scv_t (&dst)[2], int k0) {
+    f32x16_t acc[NMT][NB];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) dst[blk] = *reinterpret_cast<const scv_t*>(sb[blk] + k0 / 32);
+    for (int i = 0; i < NMT; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
+    // e8m0 bytes of 4 K steps per block (byte 4 j + 2 g + h: group 2 g + h
+    // of step j), the current chunk and the next
+    u32x4_t scn[NB], s_nxt[NB];
+    auto load_sn = [&](u32x4_t (&dst)[NB], int k0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) dst[b] = *reinterpret_cast<const u32x4_t*>(sbase[b] + k0 / 32);
     };
-    // a wave whose activation rows all lie in 32-token blocks without tokens
-    // (their MFMAs are skipped) loads nothing
-    const bool a_need = 4 * ACH * wave < 32 * NMT;
-    // accumulators of the token blocks with tokens only (the others would
-    // hold registers through the whole loop)
-    f32x16_t acc[NMT > 0 ? NMT : 1][2];
-#pragma unroll
-    for (int i = 0; i < (NMT > 0 ? NMT : 1); ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-    BRegs ring[D];
-    // J: the step's place in the unrolled group (its parity picks the LDS
-    // buffers; J % CS is its place in its scale chunk, J % D its ring slot)
     auto step = [&](auto j_tag, int ks) {
       constexpr int J = decltype(j_tag)::value;
-      const BRegs& b_use = ring[J % D];
-      BRegs& b_ld = ring[(J + D - 1) % D];
-      uint16_t* const rd = (J & 1) ? s_a1 : s_a0;
-      uint16_t* const wr = (J & 1) ? s_a0 : s_a1;
-      const int kn = min(ks + 1, nsteps - 1) * kKT;
-      const int kb = min(ks + D - 1, nsteps - 1) * kKT;
-      uint32_t sw[2];
+      const uint16_t* const rda = (J & 1) ? s_a1 : s_a0;
+      uint16_t* const wra = (J & 1) ? s_a0 : s_a1;
+      const int kn = min(ks + 1, nsteps - 1);
+      // this step's weights into registers; the next step's then go to LDS
+      u32x4_t wv[NB][2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        if constexpr (CS == 1)
-          sw[blk] = b_use.s[blk];
-        else
-          sw[blk] = scn[blk][J % CS] >> (16 * g);
-      }
-      if constexpr (D == 2) {
-        if (a_need) load_a(wr, kn);  // after the last step: unused, harmless
-        load_b(b_ld, kb);
-        if constexpr (CS > 1 && J % CS == CS - 1) {
-          if (ks + 1 < nsteps) load_sn(scn, kn);
-        }
-      } else {
-        // order: next scale chunk, activations, weights; the end-of-step wait
-        // then leaves exactly the 4 weight loads in flight
-        if constexpr (J == 0) {
-          if (ks + 4 < nsteps) load_sn(s_nxt, (ks + 4) * kKT);
-        }
-        if (a_need) load_a(wr, kn);
-        __builtin_amdgcn_sched_barrier(0);
-        load_b(b_ld, kb);
-      }
-      // keep the next step's loads at the top of this one: left to itself the
-      // scheduler sinks them behind most of the MFMAs, and the wait before
-      // the barrier then exposes their latency
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) wv[b][h] = *reinterpret_cast<const u32x4_t*>(w_lds + w_rd[b][h]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): read before the next loads overwrite
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (a_need) load_a(wra, kn);
+      load_w(kn);
+      // first step of a chunk: the scales of the chunk after this one (the
+      // end-of-step wait leaves them in flight)
+      if constexpr (J == 0) load_sn(s_nxt, min(ks + 4, nsteps - 4) * kKT);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (NMT > 0) {
-        float sc[2][2];
+      float sc[NB][2];
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          sc[blk][0] = e8m0_to_f32(sw[blk] & 0xffu);
-          sc[blk][1] = e8m0_to_f32((sw[blk] >> 8) & 0xffu);
-        }
+      for (int b = 0; b < NB; ++b) {
+        const uint32_t sw = scn[b][J] >> (16 * g);
+        sc[b][0] = e8m0_to_f32(sw & 0xffu);
+        sc[b][1] = e8m0_to_f32((sw >> 8) & 0xffu);
+      }
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          bf16x8_t af[NMT];
-          const int off = a_rd + 8 * (p ^ (xr & 7));
+      for (int p = 0; p < 8; ++p) {
+        bf16x8_t af[NMT];
+        const int off = a_rd + 8 * (p ^ (xr & 7));
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) af[mt] = *reinterpret_cast<const bf16x8_t*>(rda + 32 * mt * kKT + off);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const bf16x8_t bf = fp4_to_bf16x8(wv[b][p >> 2][p & 3], sc[b][p >> 2]);
 #pragma unroll
           for (int mt = 0; mt < NMT; ++mt)
-            af[mt] = *reinterpret_cast<const bf16x8_t*>(rd + 32 * mt * kKT + off);
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk) {
-            const bf16x8_t bf = fp4_to_bf16x8(b_use.c[blk][p >> 2][p & 3], sc[blk][p >> 2]);
-#pragma unroll
-            for (int mt = 0; mt < NMT; ++mt)
-              acc[mt][blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf, acc[mt][blk], 0, 0, 0);
-          }
+            acc[mt][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bf, acc[mt][b], 0, 0, 0);
         }
       }
-      if constexpr (D == 4 && J == 3) {
-        scn[0] = s_nxt[0];
-        scn[1] = s_nxt[1];
+      if constexpr (J == 3) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) scn[b] = s_nxt[b];
       }
-      if constexpr (D == 2) {
-        vmem_wait_all();  // this wave's direct-to-LDS loads (and the next weights) have landed
-        lds_barrier();
-      } else {
-        barrier_keep4();  // all but this step's 4 weight loads: the activations have landed
-      }
+      // the next step's operands have landed (J == 0: all but the NB scale
+      // loads)
+      barrier_keep<J == 0 ? NB : 0>();
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
-#pragma unroll
-    for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(i, nsteps - 1) * kKT);
-    if constexpr (CS > 1) load_sn(scn, 0);
+    load_sn(scn, 0);
     if (a_need) load_a(s_a0, 0);
+    load_w(0);
     vmem_wait_all();
     lds_barrier();
-    if constexpr (CS == 2) {  // nsteps % 2 == 0
-      for (int ks = 0; ks < nsteps; ks += 2) {
-        step(I0{}, ks);
-        step(I1{}, ks + 1);
-      }
-    } else if constexpr (CS == 4) {  // nsteps % 4 == 0
-      for (int ks = 0; ks < nsteps; ks += 4) {
-        step(I0{}, ks);
-        step(I1{}, ks + 1);
-        step(I2{}, ks + 2);
-        step(I3{}, ks + 3);
-      }
-    } else {
-      int ks = 0;
-      for (; ks + 2 <= nsteps; ks += 2) {
-        step(I0{}, ks);
-        step(I1{}, ks + 1);
-      }
-      if (ks < nsteps) step(I0{}, ks);
+    for (int ks = 0; ks < nsteps; ks += 4) {
+      step(I0{}, ks);
+      step(I1{}, ks + 1);
+      step(I2{}, ks + 2);
+      step(I3{}, ks + 3);
     }
 
     // epilogue: element i of lane l is token 32 mt + 8 (i / 4) + 4 g + i % 4
@@ -582,27 +553,27 @@ __global__ __launch_bounds__(64 * kMxwWaves, 8 / kMxwWaves) void k_mfma_mxfp4_w(
         const int tl = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
         if (tl >= count) continue;
         if constexpr (GATEUP) {
-          a.h[static_cast<size_t>(p0 + tl) * rows + row0] =
+          a.h[static_cast<size_t>(p0 + tl) * rows + wrow(0) + r32] =
               static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mt][0][i]) * acc[mt][1][i]));
         } else {
           const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
-          float* yrow = a.y + static_cast<size_t>(slot) * rows + row0;
-          yrow[0] = acc[mt][0][i];
-          yrow[32] = acc[mt][1][i];
+          float* yrow = a.y + static_cast<size_t>(slot) * rows;
+#pragma unroll
+          for (int b = 0; b < NB; ++b) yrow[wrow(b) + r32] = acc[mt][b][i];
         }
       }
     }
   };
-  using D2 = std::integral_constant<int, 2>;
-  using D4 = std::integral_constant<int, SCS == 4 ? 4 : 2>;
   switch (nmt) {
-    case 4: kloop(std::integral_constant<int, 4>{}, D2{}); break;
-    case 3: kloop(std::integral_constant<int, 3>{}, D2{}); break;
-    case 2: kloop(std::integral_constant<int, 2>{}, D4{}); break;
-    case 1: kloop(std::integral_constant<int, 1>{}, D4{}); break;
-    default: kloop(std::integral_constant<int, 0>{}, D2{}); break;
+    case 4: kloop(std::integral_constant<int, 4>{}); break;
+    case 3: kloop(std::integral_constant<int, 3>{}); break;
+    case 2: kloop(std::integral_constant<int, 2>{}); break;
+    default: kloop(std::integral_constant<int, 1>{}); break;
   }
 }
+
+// LDS of k_mfma_mxfp4_w: two activation buffers and the 4 waves' weight rows
+constexpr size_t kMxwLds = 2 * 128 * kKT * 2 + 4 * 64 * 64;
 
 // ---------------------------------------------------------------------------
 // Affine b-bit experts, b in {2, 3, 4} (w = s q + b per group of G inputs,
@@ -1108,23 +1079,14 @@ static void launch_affine(const MfmaArgs& a, hipStream_t s) {
 template <bool GATEUP>
 static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
   const QMat& m = a.m0;
-  constexpr int kMxwN = (GATEUP ? 32 : 64) * kMxwWaves;  // k_mfma_mxfp4_w's rows per workgroup
-  if (m.fmt == 1 && m.rows % kMxwN == 0) {
-    const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
-    const dim3 grid(mfma_grid(a.T, a.k, a.E, m.rows, kMxwN, 128));
-    // scale loads of c steps (4 c bytes) need rows of whole chunks on aligned scale arrays
-    auto chunks = [&](int c) {
-      return c <= kMxfp4ScaleSteps && m.cols % (c * kKT) == 0 &&
-             reinterpret_cast<uintptr_t>(a.m0.scales) % (4 * c) == 0 &&
-             reinterpret_cast<uintptr_t>(a.m1.scales) % (4 * c) == 0;
-    };
-    const dim3 block(64 * kMxwWaves);
-    if (chunks(4))
-      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 4>), grid, block, lds, s, a);
-    else if (chunks(2))
-      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 2>), grid, block, lds, s, a);
-    else
-      QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP, 1>), grid, block, lds, s, a);
+  constexpr int kMxwN = GATEUP ? 128 : 256;  // k_mfma_mxfp4_w's rows per workgroup (per matrix)
+  if (m.fmt == 1 && m.rows % kMxwN == 0 && m.cols % (4 * kKT) == 0 && 2 * (a.E + 1) * 4 <= 4 * 64 * 64 &&
+      reinterpret_cast<uintptr_t>(a.m0.scales) % 16 == 0 && reinterpret_cast<uintptr_t>(a.m1.scales) % 16 == 0) {
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mfma_mxfp4_w<GATEUP>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMxwLds);
+    if (attr != hipSuccess) return attr;
+    QSMOE_LAUNCH((k_mfma_mxfp4_w<GATEUP>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, kMxwN, 128)), dim3(256), kMxwLds, s,
+                 a);
   } else if (m.fmt == 1) {
     // measured: gate/up best with 128-token tiles x 32 columns per wave, down
     // with 64-token tiles x 64 columns per wave
