@@ -112,16 +112,19 @@ def kernel_bytes(name, cfg, dl, T, touched):
         return T * d * (4 + 4)
     if name == "combine":
         return tk * d * 4 + tk * 4 + (T * d * 4 if sh is not None else 0) + T * d * 2
-    # fused small-batch path
+    # fused small-batch path (a single token streams the shared expert's down
+    # rows in its gate/up launch)
     sh_gu = sh.gate.nbytes_per_expert() + sh.up.nbytes_per_expert() + T * cfg.I_shared * 2 if sh is not None else 0
     sh_dn = sh.down.nbytes_per_expert() + T * cfg.I_shared * 2 if sh is not None else 0
+    sh_dn_in_gu = T == 1 and d <= 4096
+    gu = touched * (r.gate.nbytes_per_expert() + r.up.nbytes_per_expert()) + T * E * 12 + T * d * 2 + tk * I * 2
     if name == "dec_router":
         return E * d * 4 + T * d * 2 + T * E * 16 + sh_gu
     if name == "dec_gateup":
-        return (touched * (r.gate.nbytes_per_expert() + r.up.nbytes_per_expert()) + T * E * 12 + T * d * 2
-                + tk * I * 2 + tk * 8)
+        return gu + tk * 8 + (sh_dn + T * d * 4 if sh_dn_in_gu else 0)
     if name == "dec_down_combine":
-        return touched * r.down.nbytes_per_expert() + sh_dn + T * E * 4 + tk * I * 2 + T * d * 2
+        sh_part = T * d * 4 if sh_dn_in_gu else sh_dn
+        return touched * r.down.nbytes_per_expert() + sh_part + T * E * 4 + tk * I * 2 + T * d * 2
     raise KeyError(name)
 
 
