@@ -46,6 +46,14 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// The same with the division as a reciprocal (at most ~3 fp32 ulps apart,
+// 8 fewer instructions); below z = -64, where the reciprocal of 1 + e^-z
+// would leave the normal range, the exact division.
+__device__ __forceinline__ float silu_fast(float z) {
+  const float d = 1.0f + expf(-z);
+  if (z > -64.0f) return z * __builtin_amdgcn_rcpf(d);
+  return z / d;
+}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,

@@ -554,7 +554,7 @@ __global__ __launch_bounds__(256, 2) void k_mfma_mxfp4_w(MfmaArgs a) {
         if (tl >= count) continue;
         if constexpr (GATEUP) {
           a.h[static_cast<size_t>(p0 + tl) * rows + wrow(0) + r32] =
-              static_cast<uint16_t>(f32_to_bf16_rne(silu(acc[mt][0][i]) * acc[mt][1][i]));
+              static_cast<uint16_t>(f32_to_bf16_rne(silu_fast(acc[mt][0][i]) * acc[mt][1][i]));
         } else {
           const int slot = a.shared ? p0 + tl : min(max(a.perm[p0 + tl], 0), n - 1);
           float* yrow = a.y + static_cast<size_t>(slot) * rows;
