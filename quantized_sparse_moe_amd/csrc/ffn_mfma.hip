@@ -684,7 +684,16 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2][MT][kALdsStride];
   // weight macro steps: ROWB bytes of each of a wave's 64 rows
   constexpr int QW = BITS == 8 ? 2 : 1;         // words per 8-code chunk as read
-  constexpr float kOff = BITS == 8 ? 0.0f : static_cast<float>(1 << BITS);  // value of code 0 as decoded
+  // 2-bit codes in groups of 64 or 128 decode through the e2m1 converter:
+  // a code q in the low two bits of a nibble is the e2m1 value q / 2, so
+  // with the conversion's scale 2 each masked nibble pair becomes the exact
+  // bf16 pair (q, q') with no code offset. A 32-bit word of 16 codes serves
+  // two passes of a lane group (its even-indexed codes, then its odd ones),
+  // so a pass covers inputs 64 t + 16 g + (0, 2, .., 14) or (1, 3, .., 15):
+  // 64 inputs, one group. The activations are stored in LDS in that order
+  // (each 16-input block as its 8 even-indexed then its 8 odd-indexed inputs).
+  constexpr bool CVT2 = BITS == 2 && G >= 64 && FMT == 0;
+  constexpr float kOff = (BITS == 8 || CVT2) ? 0.0f : static_cast<float>(1 << BITS);  // value of code 0 as decoded
   constexpr int LPR = 8;                        // lanes per row in one load
   constexpr int BPL = BITS == 3 ? 12 : 16;      // bytes per lane in one load
   constexpr int ROWB = LPR * BPL;               // bytes per row per macro step
@@ -729,8 +738,21 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
   };
   auto store_a = [&](const u32x4_t (&ar)[ACH], int buf) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i)
-      *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row[i]][a_chunk * 8]) = interleave_halves(ar[i]);
+    for (int i = 0; i < ACH; ++i) {
+      if constexpr (CVT2) {
+        // inputs 8 c .. 8 c + 7 (c = a_chunk): half c % 2 of 16-input block c / 2
+        const u32x4_t v = ar[i];
+        const uint32_t e0 = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+        const uint32_t e1 = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+        const uint32_t o0 = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+        const uint32_t o1 = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+        uint16_t* blk = &s_a[buf][a_row[i]][16 * (a_chunk >> 1) + 4 * (a_chunk & 1)];
+        *reinterpret_cast<uint2*>(blk) = make_uint2(e0, e1);
+        *reinterpret_cast<uint2*>(blk + 8) = make_uint2(o0, o1);
+      } else {
+        *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row[i]][a_chunk * 8]) = interleave_halves(ar[i]);
+      }
+    }
   };
 
   // weights: wave row R (0..63) is row rbase0 + 16 (R / 16 % HB) + R % 16 of
@@ -811,6 +833,10 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
       c[QW - 1] = v.y;
     } else if constexpr (BITS == 4) {
       c[0] = *reinterpret_cast<const uint32_t*>(row + 4 * (16 * jm + 4 * s + g));
+    } else if constexpr (CVT2) {
+      // passes 2 t, 2 t + 1 (t = s / 2) share the word of codes
+      // 64 t + 16 g .. + 15 of the step
+      c[0] = *reinterpret_cast<const uint32_t*>(row + 32 * jm + 16 * (s >> 1) + 4 * g);
     } else if constexpr (BITS == 2) {
       // codes 0..3 in byte 0, 4..7 in byte 1 -> bytes 0 and 2
       const uint32_t h = *reinterpret_cast<const uint16_t*>(row + 2 * (16 * jm + 4 * s + g));
@@ -890,7 +916,9 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) read_chunk(rb, s, JM, qw[rb][s]);
+        for (int s = 0; s < 4; ++s) {
+          if (!CVT2 || (s & 1) == 0) read_chunk(rb, s, JM, qw[rb][s]);  // CVT2: one word per two passes
+        }
       // this step's scales and biases live in lane group J % 4
       uint32_t sw[RB][SWS], bw[RB][SWS];
 #pragma unroll
@@ -934,8 +962,10 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
           const int s = j * PPG + pp;
           bf16x8_t af[NMB];
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb)
-            af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][mb * 16 + r16][32 * s + 8 * g]);
+          for (int mb = 0; mb < NMB; ++mb) {
+            const int ao = CVT2 ? 64 * (s >> 1) + 16 * g + 8 * (s & 1) : 32 * s + 8 * g;
+            af[mb] = *reinterpret_cast<const bf16x8_t*>(&s_a[buf][mb * 16 + r16][ao]);
+          }
           if constexpr (FMT == 0) {
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
@@ -945,10 +975,19 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) {
             bf16x8_t bf;
-            if constexpr (FMT == 2)
+            if constexpr (FMT == 2) {
               bf = e4m3_chunk_to_bf16x8(qw[rb][s]);
-            else
+            } else if constexpr (CVT2) {
+              const uint32_t w = qw[rb][s & ~1][0];
+              const uint32_t m = ((s & 1) ? (w >> 2) : w) & 0x33333333u;
+              const u32x4_t r{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 0)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 1)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 2)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 3))};
+              bf = __builtin_bit_cast(bf16x8_t, r);
+            } else {
               bf = chunk_to_bf16x8<BITS>(qw[rb][s]);
+            }
 #pragma unroll
             for (int mb = 0; mb < NMB; ++mb)
               dg[j][mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
