@@ -65,21 +65,28 @@ struct Codec<0, 4> {
 // Affine 2-bit: word j holds codes 16j..16j+15; pair m = 8j + i is (16j+i, 16j+i+8).
 template <>
 struct Codec<0, 2> {
-  static constexpr float kOff = 4.0f;
-  static constexpr int lo(int m) { return 16 * (m >> 3) + (m & 7); }
-  static constexpr int hi(int m) { return lo(m) + 8; }
+  // A 2-bit code q in the low two bits of a nibble is the e2m1 value q / 2:
+  // masking word j with 0x33333333 leaves its even-indexed codes in the
+  // nibbles (its odd-indexed ones after a shift by 2), and
+  // v_cvt_scalef32_pk_bf16_fp4 at scale 2 turns each byte into the exact bf16
+  // pair of its two codes (3 masks and 8 conversions per 16 codes; no code
+  // offset). Pair m = 8j + r is (16j + 4r, 16j + 4r + 2) for r < 4 and
+  // (16j + 4(r - 4) + 1, 16j + 4(r - 4) + 3) for r >= 4.
+  static constexpr float kOff = 0.0f;
+  static constexpr int lo(int m) { return 16 * (m >> 3) + 4 * (m & 3) + ((m >> 2) & 1); }
+  static constexpr int hi(int m) { return lo(m) + 2; }
   __device__ static __forceinline__ void pairs(const uint32_t (&w)[2], uint32_t (&p)[16]) {
-    const uint32_t k = code_base_pair<2>();
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      p[8 * j + 0] = code_pair<2, 0>(w[j], k);
-      p[8 * j + 1] = code_pair<2, 2>(w[j], k);
-      p[8 * j + 2] = code_pair<2, 4>(w[j], k);
-      p[8 * j + 3] = code_pair<2, 6>(w[j], k);
-      p[8 * j + 4] = code_pair<2, 8>(w[j], k);
-      p[8 * j + 5] = code_pair<2, 10>(w[j], k);
-      p[8 * j + 6] = code_pair<2, 12>(w[j], k);
-      p[8 * j + 7] = code_pair<2, 14>(w[j], k);
+      const uint32_t m0 = w[j] & 0x33333333u, m1 = (w[j] >> 2) & 0x33333333u;
+#define QSMOE_CVT2(K_)                                                                                        \
+  p[8 * j + K_] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m0, 2.0f, K_));     \
+  p[8 * j + 4 + K_] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m1, 2.0f, K_));
+      QSMOE_CVT2(0)
+      QSMOE_CVT2(1)
+      QSMOE_CVT2(2)
+      QSMOE_CVT2(3)
+#undef QSMOE_CVT2
     }
   }
 };

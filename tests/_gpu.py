@@ -149,7 +149,11 @@ def check_weights_exact(scores, ids, w, routed_scale=1.0):
 def _abs_terms(q, e):
     """|terms| the kernels sum per weight, as a [rows][cols] float64 bound:
     affine b <= 4 codes are summed as 2^b + q with the bias term b - 2^b s
-    (8-bit: q with b), so |s| (off + q) + |b - off s|; MX formats |w|."""
+    (8-bit: q with b), so |s| (off + q) + |b - off s|; MX formats |w|.
+    2-bit codes are summed as q with b on the streaming and fused paths and
+    in the grouped GEMM with groups of 64 or 128; the 2^b form kept here
+    bounds those terms too, since |b| <= |b - 4 s| + 4 |s| gives
+    |s| q + |b| <= |s| (4 + q) + |b - 4 s|."""
     spec = q.spec
     if spec.fmt == "affine":
         off = float(2 ** spec.bits) if spec.bits <= 4 else 0.0
