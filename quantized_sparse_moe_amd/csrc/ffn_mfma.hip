@@ -579,10 +579,12 @@ constexpr size_t kMxwLds = 2 * 128 * kKT * 2 + 4 * 64 * 64;
 // Affine b-bit experts, b in {2, 3, 4} (w = s q + b per group of G inputs,
 // fp16 s and b).
 //
-// Codes become exact bf16 without a multiply: the code in the top bits of
-// the mantissa of 2^b gives the value off + q, off = 2^b (code_pair). Each
-// MFMA pass covers 32 consecutive inputs, so all of them lie in one group per
-// output row, and per group the kernel gets
+// Codes become exact bf16 without a multiply: 3-bit codes in the top bits of
+// the mantissa of 2^b give the value off + q, off = 2^b (code_pair); 4-bit
+// and 2-bit codes go through the e4m3 and e2m1 converters and give q itself
+// (off = 0; see CVT4 and CVT2 below). Each MFMA pass covers 32 consecutive
+// inputs, so all of them lie in one group per output row, and per group the
+// kernel gets
 //   D[m][n] = sum_k x[m][k] (off + q[n][k])   and   X[m] = sum_k x[m][k]
 // (X from an extra MFMA against a B operand of ones), then adds
 //   s[n] D[m][n] + (b[n] - off s[n]) X[m]
@@ -693,7 +695,15 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
   // 64 inputs, one group. The activations are stored in LDS in that order
   // (each 16-input block as its 8 even-indexed then its 8 odd-indexed inputs).
   constexpr bool CVT2 = BITS == 2 && G >= 64 && FMT == 0;
-  constexpr float kOff = (BITS == 8 || CVT2) ? 0.0f : static_cast<float>(1 << BITS);  // value of code 0 as decoded
+  // 4-bit codes decode through the e4m3 converter: a byte q in 0..15 is the
+  // E4M3 value q 2^-9 (subnormal below 8, exponent 1 from 8 on), so with the
+  // conversion's scale 2^9 the nibbles of a chunk word, masked into bytes
+  // (even-indexed codes, then after a shift by 4 the odd ones), become the
+  // exact bf16 values q with no code offset: the chunk's 8 codes in the order
+  // (0, 2, 4, 6, 1, 3, 5, 7), and the activations are stored in LDS in that
+  // order within each 8-input chunk.
+  constexpr bool CVT4 = BITS == 4 && FMT == 0;
+  constexpr float kOff = (BITS == 8 || CVT2 || CVT4) ? 0.0f : static_cast<float>(1 << BITS);  // value of code 0 as decoded
   constexpr int LPR = 8;                        // lanes per row in one load
   constexpr int BPL = BITS == 3 ? 12 : 16;      // bytes per lane in one load
   constexpr int ROWB = LPR * BPL;               // bytes per row per macro step
@@ -749,6 +759,12 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
         uint16_t* blk = &s_a[buf][a_row[i]][16 * (a_chunk >> 1) + 4 * (a_chunk & 1)];
         *reinterpret_cast<uint2*>(blk) = make_uint2(e0, e1);
         *reinterpret_cast<uint2*>(blk + 8) = make_uint2(o0, o1);
+      } else if constexpr (CVT4) {
+        // inputs 8 c .. 8 c + 7 as (0, 2, 4, 6, 1, 3, 5, 7)
+        const u32x4_t v = ar[i];
+        *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row[i]][a_chunk * 8]) =
+            u32x4_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u), __builtin_amdgcn_perm(v[3], v[2], 0x05040100u),
+                    __builtin_amdgcn_perm(v[1], v[0], 0x07060302u), __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
       } else {
         *reinterpret_cast<u32x4_t*>(&s_a[buf][a_row[i]][a_chunk * 8]) = interleave_halves(ar[i]);
       }
@@ -947,7 +963,8 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
             continue;
           }
           const float sc = f16_to_f32(static_cast<uint16_t>(sw[rb][j / 2] >> (16 * (j & 1))));
-          const float bc = fmaf(-kOff, sc, f16_to_f32(static_cast<uint16_t>(bw[rb][j / 2] >> (16 * (j & 1)))));
+          const float bb = f16_to_f32(static_cast<uint16_t>(bw[rb][j / 2] >> (16 * (j & 1))));
+          const float bc = kOff == 0.0f ? bb : fmaf(-kOff, sc, bb);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
@@ -984,6 +1001,15 @@ __global__ __launch_bounds__(256, (aff_min_wg<GATEUP, BITS, G, MT>())) void k_mf
                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 1)),
                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 2)),
                               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, 3))};
+              bf = __builtin_bit_cast(bf16x8_t, r);
+            } else if constexpr (CVT4) {
+              const uint32_t w = qw[rb][s][0];
+              const uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;
+              const u32x4_t r{
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, 512.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, 512.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, 512.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, 512.0f, true))};
               bf = __builtin_bit_cast(bf16x8_t, r);
             } else {
               bf = chunk_to_bf16x8<BITS>(qw[rb][s]);
