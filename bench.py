@@ -208,7 +208,7 @@ def _fmt_tag(f, gateup):
     if f.fmt == "mxfp4":
         return f"k_mfma_mxfp4"
     if f.fmt == "mxfp8":
-        return f"k_mfma_affine<{gu}, 8, 32, 16, 2>"
+        return f"k_mfma_affine<{gu}, 8, 32, "  # 16- or 32-token tiles, format 2 (checked below)
     return f"k_mfma_affine<{gu}, {f.bits}, "
 
 
@@ -227,6 +227,8 @@ def kernel_matches(label, cfg, key):
         tag = _fmt_tag(f, gateup)
         if f.fmt == "mxfp4":
             return key.startswith(tag) and ("<true" in key) == gateup
+        if f.fmt == "mxfp8":
+            return key.startswith(tag) and key.endswith(", 2>")
         return key.startswith(tag)
     if label in ("routed_gateup", "routed_down"):
         gateup = label == "routed_gateup"

@@ -1169,8 +1169,15 @@ static hipError_t launch_mfma(const MfmaArgs& a, hipStream_t s) {
     // MXFP8: the 8-bit affine layout with E4M3 decode and e8m0 group scales
     constexpr int NTILE = (GATEUP ? 32 : 64) * kAffRB;
     const size_t lds = static_cast<size_t>(2) * (a.E + 1) * sizeof(int32_t);
-    QSMOE_LAUNCH((k_mfma_affine<GATEUP, 8, 32, 16, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, 16, a.ksplit)),
-                 dim3(256), lds, s, a);
+    // 32-token tiles from 8 tokens per expert on average, as for the affine
+    // codes (no bias term here, so groups of 32 fit the larger tile: 223
+    // VGPRs; measured at 512 tokens: gate/up 830 -> 691 us, down 464 -> 437 us)
+    if (static_cast<int64_t>(a.T) * a.k < 8LL * a.E)
+      QSMOE_LAUNCH((k_mfma_affine<GATEUP, 8, 32, 16, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, 16, a.ksplit)),
+                   dim3(256), lds, s, a);
+    else
+      QSMOE_LAUNCH((k_mfma_affine<GATEUP, 8, 32, 32, 2>), dim3(mfma_grid(a.T, a.k, a.E, m.rows, NTILE, 32, a.ksplit)),
+                   dim3(256), lds, s, a);
   } else if (m.bits == 2) {
     launch_affine<GATEUP, 2, 16>(a, s);
   } else if (m.bits == 3) {

@@ -148,6 +148,8 @@ def test_rocprof_names_match_probe_labels_by_format():
     assert m("routed_gateup_mfma", prefill, "k_mfma_mxfp4_w<true, 4>")
     assert not m("routed_gateup_mfma", prefill, "k_mfma_mxfp4_w<false, 4>")
     assert m("routed_down_mfma", mx8, "k_mfma_affine<false, 8, 32, 16, 2>")
+    assert m("routed_gateup_mfma", mx8, "k_mfma_affine<true, 8, 32, 32, 2>")
+    assert not m("routed_gateup_mfma", mx8, "k_mfma_affine<true, 8, 32, 32, 0>")
     assert m("routed_gateup", mixed, "k_ffn_stream<0, 2, 2, 1, true>")
     assert not m("routed_gateup", mixed, "k_ffn_stream<0, 8, 2, 1, true>")
     assert m("dec_gateup", mixed, "k_dec_gateup1<0, 2, 2>") and m("dec_router", mixed, "k_dec_router<1, 2, 1>")
